@@ -1,0 +1,353 @@
+/*
+ * pav2_oracle.c -- plain, slow, float64 CPU oracle for PagedAttention V2 decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header or constant with the HIP
+ * library.
+ *
+ * What it computes, step by step, in the order of the pages (source page
+ * "paged_attention_v2_pytorch.py", function paged_attention_v2_pytorch):
+ *
+ *   0. Unused partition slots: max_logits = -inf, exp_sums = 0, tmp_output = 0
+ *      (the "Initialize unused slots" block).
+ *   1. seq_len == 0 gives a zero output row (the seq_len == 0 early continue).
+ *   2. Paged gather (the "Batched KV gather" block):
+ *        block  = block_tables[s, t / block_size]
+ *        K[t,i] = key_cache  [block, kv_head, i / x, t % block_size, i % x]
+ *        V[t,i] = value_cache[block, kv_head, i,     t % block_size]
+ *      then K *= k_scale, V *= v_scale after widening.
+ *   3. GQA without expansion: query head h reads kv head h / (H / kv_h)
+ *      (the "GQA broadcast" block views q as [kv_h, gqa, 1, d]).
+ *   4. Scores z_t = scale * (q . K_t), plus alibi_slopes[h] * t with t the
+ *      absolute 0-based position (the "Alibi bias" block).
+ *   5. Per 512-token partition p (the padded reshape to [H, P, 512]):
+ *        m_p = max z, e_t = exp(z_t - m_p), l_p = sum e_t,
+ *        o_p = sum e_t V_t / l_p.
+ *      The page stores sum e_t V_t without the division by l_p, but its own
+ *      phase-2 combine (and the Triton reduce on page 2) weight the partition
+ *      outputs by exp(m_p - M) * l_p / sum, which reproduces softmax(z) V only
+ *      for the normalised o_p; the normalised reading is the one taken here.
+ *   6. Phase 2 (the "Cross-partition reduction" block):
+ *        M = max_p m_p, w_p = exp(m_p - M) * l_p, out = sum_p w_p o_p / sum_p w_p.
+ *
+ * A second entry point computes the unpartitioned result, one softmax over
+ * all tokens (the single-pass online-softmax decode on page 3,
+ * "paged_attn.py", _forward_decode_pytorch, reaches the same value), for
+ * invariant tests.
+ *
+ * Element decoding is exact widening to double, written from the formats'
+ * definitions: IEEE-754 binary32 and binary16, bfloat16 (the upper half of a
+ * binary32), and OCP 8-bit E4M3 ("e4m3fn": bias 7, no infinities, S.1111.111
+ * is NaN).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_FP8_E4M3 = 3 };
+
+#define OR_PARTITION 512
+
+static int elem_size(int dtype) {
+    switch (dtype) {
+    case OR_F32: return 4;
+    case OR_F16: return 2;
+    case OR_BF16: return 2;
+    case OR_FP8_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+/* ---- element decoding (exact) ---------------------------------------- */
+
+static double dec_f32(uint32_t bits) {
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+}
+
+static double dec_f16(uint16_t bits) {
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 10) & 0x1f;
+    int m = bits & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)m, -24);               /* subnormal: m * 2^-24 */
+    } else if (e == 31) {
+        v = (m == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(1024 + m), e - 25);  /* (1 + m/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+static double dec_bf16(uint16_t bits) {
+    return dec_f32((uint32_t)bits << 16);
+}
+
+static double dec_fp8_e4m3(uint8_t bits) {
+    int sign = (bits >> 7) & 1;
+    int e = (bits >> 3) & 0xf;
+    int m = bits & 0x7;
+    double v;
+    if (e == 15 && m == 7) {
+        v = NAN;
+    } else if (e == 0) {
+        v = ldexp((double)m, -9);               /* subnormal: (m/8) * 2^-6 */
+    } else {
+        v = ldexp((double)(8 + m), e - 10);     /* (1 + m/8) * 2^(e-7) */
+    }
+    return sign ? -v : v;
+}
+
+static double dec(int dtype, const void *base, int64_t idx) {
+    const uint8_t *p = (const uint8_t *)base;
+    switch (dtype) {
+    case OR_F32: {
+        uint32_t b;
+        memcpy(&b, p + 4 * idx, 4);
+        return dec_f32(b);
+    }
+    case OR_F16: {
+        uint16_t b;
+        memcpy(&b, p + 2 * idx, 2);
+        return dec_f16(b);
+    }
+    case OR_BF16: {
+        uint16_t b;
+        memcpy(&b, p + 2 * idx, 2);
+        return dec_bf16(b);
+    }
+    case OR_FP8_E4M3:
+        return dec_fp8_e4m3(p[idx]);
+    default:
+        return NAN;
+    }
+}
+
+/* Decode n elements of one dtype into doubles (exposed so tests can check
+ * the decoders against library conversions of every code). */
+int oracle_decode(int dtype, const void *src, int64_t n, double *dst) {
+    if (elem_size(dtype) == 0) return -1;
+    for (int64_t i = 0; i < n; ++i) dst[i] = dec(dtype, src, i);
+    return 0;
+}
+
+/* ---- problem description --------------------------------------------- */
+
+typedef struct {
+    const void *query;          /* [S, H, D] q_dtype */
+    const void *key_cache;      /* [NB, KVH, D/x, BS, x] kv_dtype */
+    const void *value_cache;    /* [NB, KVH, D, BS] kv_dtype */
+    const int32_t *block_tables;/* [S, MBPS] */
+    const int32_t *seq_lens;    /* [S] */
+    const float *alibi_slopes;  /* [H] or NULL */
+    int q_dtype, kv_dtype;
+    int num_seqs, num_heads, num_kv_heads, head_size, block_size;
+    int max_blocks_per_seq, max_num_partitions;
+    float scale, k_scale, v_scale;
+    /* outputs, float64 */
+    double *out;                /* [S, H, D] */
+    double *max_logits;         /* [S, H, maxP] (partitioned entry only) */
+    double *exp_sums;           /* [S, H, maxP] */
+    double *tmp_out;            /* [S, H, maxP, D] */
+    const uint8_t *pair_mask;   /* [S*H] or NULL: which (s, h) to compute */
+    int dense;                  /* 1: unpartitioned softmax, 0: V2 partitioned */
+    int next_pair;              /* work counter shared by the threads */
+} problem_t;
+
+/* Key element i of logical token t of sequence s, kv head g (step 2). */
+static double key_at(const problem_t *P, int s, int g, int t, int i) {
+    int x = 16 / elem_size(P->kv_dtype);
+    int bs = P->block_size;
+    int64_t blk = P->block_tables[(int64_t)s * P->max_blocks_per_seq + t / bs];
+    int64_t idx = ((((blk * P->num_kv_heads + g) * (P->head_size / x) + i / x) * bs + t % bs) * x) + i % x;
+    return dec(P->kv_dtype, P->key_cache, idx) * (double)P->k_scale;
+}
+
+/* Value element i of logical token t of sequence s, kv head g (step 2). */
+static double value_at(const problem_t *P, int s, int g, int t, int i) {
+    int bs = P->block_size;
+    int64_t blk = P->block_tables[(int64_t)s * P->max_blocks_per_seq + t / bs];
+    int64_t idx = (((blk * P->num_kv_heads + g) * P->head_size + i) * bs) + t % bs;
+    return dec(P->kv_dtype, P->value_cache, idx) * (double)P->v_scale;
+}
+
+/* Scores z_t for t in [0, L) of query head h (steps 3 and 4). */
+static void scores(const problem_t *P, int s, int h, int L, double *z) {
+    int D = P->head_size;
+    int gqa = P->num_heads / P->num_kv_heads;
+    int g = h / gqa;
+    double slope = P->alibi_slopes ? (double)P->alibi_slopes[h] : 0.0;
+    for (int t = 0; t < L; ++t) {
+        double dot = 0.0;
+        for (int i = 0; i < D; ++i) {
+            double q = dec(P->q_dtype, P->query, ((int64_t)s * P->num_heads + h) * D + i);
+            dot += q * key_at(P, s, g, t, i);
+        }
+        z[t] = dot * (double)P->scale;
+        if (P->alibi_slopes) z[t] += slope * (double)t;
+    }
+}
+
+static void solve_pair(const problem_t *P, int s, int h, double *z, double *e) {
+    int D = P->head_size;
+    int maxP = P->max_num_partitions;
+    int gqa = P->num_heads / P->num_kv_heads;
+    int g = h / gqa;
+    int L = P->seq_lens[s];
+    double *out = P->out + ((int64_t)s * P->num_heads + h) * D;
+
+    if (!P->dense) {
+        double *ml = P->max_logits + ((int64_t)s * P->num_heads + h) * maxP;
+        double *es = P->exp_sums + ((int64_t)s * P->num_heads + h) * maxP;
+        double *to = P->tmp_out + ((int64_t)s * P->num_heads + h) * maxP * D;
+        /* step 0: every slot starts unused */
+        for (int p = 0; p < maxP; ++p) {
+            ml[p] = -INFINITY;
+            es[p] = 0.0;
+            for (int i = 0; i < D; ++i) to[(int64_t)p * D + i] = 0.0;
+        }
+        if (L == 0) {                                   /* step 1 */
+            for (int i = 0; i < D; ++i) out[i] = 0.0;
+            return;
+        }
+        scores(P, s, h, L, z);                          /* steps 2-4 */
+        int nparts = (L + OR_PARTITION - 1) / OR_PARTITION;
+        for (int p = 0; p < nparts; ++p) {              /* step 5 */
+            int t0 = p * OR_PARTITION;
+            int t1 = t0 + OR_PARTITION < L ? t0 + OR_PARTITION : L;
+            double m = -INFINITY;
+            for (int t = t0; t < t1; ++t) m = z[t] > m ? z[t] : m;
+            double l = 0.0;
+            for (int t = t0; t < t1; ++t) {
+                e[t] = exp(z[t] - m);
+                l += e[t];
+            }
+            for (int i = 0; i < D; ++i) {
+                double acc = 0.0;
+                for (int t = t0; t < t1; ++t) acc += e[t] * value_at(P, s, g, t, i);
+                to[(int64_t)p * D + i] = acc / l;
+            }
+            ml[p] = m;
+            es[p] = l;
+        }
+        double M = -INFINITY;                           /* step 6 */
+        for (int p = 0; p < nparts; ++p) M = ml[p] > M ? ml[p] : M;
+        double W = 0.0;
+        for (int p = 0; p < nparts; ++p) W += exp(ml[p] - M) * es[p];
+        for (int i = 0; i < D; ++i) {
+            double acc = 0.0;
+            for (int p = 0; p < nparts; ++p)
+                acc += exp(ml[p] - M) * es[p] * to[(int64_t)p * D + i];
+            out[i] = acc / W;
+        }
+    } else {
+        if (L == 0) {
+            for (int i = 0; i < D; ++i) out[i] = 0.0;
+            return;
+        }
+        scores(P, s, h, L, z);
+        double M = -INFINITY;
+        for (int t = 0; t < L; ++t) M = z[t] > M ? z[t] : M;
+        double W = 0.0;
+        for (int t = 0; t < L; ++t) {
+            e[t] = exp(z[t] - M);
+            W += e[t];
+        }
+        for (int i = 0; i < D; ++i) {
+            double acc = 0.0;
+            for (int t = 0; t < L; ++t) acc += e[t] * value_at(P, s, g, t, i);
+            out[i] = acc / W;
+        }
+    }
+}
+
+static void *worker(void *arg) {
+    problem_t *P = (problem_t *)arg;
+    int max_len = 0;
+    for (int s = 0; s < P->num_seqs; ++s) max_len = P->seq_lens[s] > max_len ? P->seq_lens[s] : max_len;
+    double *z = (double *)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    double *e = (double *)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    int npairs = P->num_seqs * P->num_heads;
+    for (;;) {
+        int k = __atomic_fetch_add(&P->next_pair, 1, __ATOMIC_RELAXED);
+        if (k >= npairs) break;
+        if (P->pair_mask && !P->pair_mask[k]) continue;
+        solve_pair(P, k / P->num_heads, k % P->num_heads, z, e);
+    }
+    free(z);
+    free(e);
+    return NULL;
+}
+
+static int run(problem_t *P, int num_threads) {
+    if (elem_size(P->q_dtype) == 0 || elem_size(P->kv_dtype) == 0) return -1;
+    if (P->num_kv_heads <= 0 || P->num_heads % P->num_kv_heads != 0) return -1;
+    if (P->head_size % (16 / elem_size(P->kv_dtype)) != 0) return -1;
+    if (P->block_size <= 0) return -1;
+    P->next_pair = 0;
+    if (num_threads < 1) num_threads = 1;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)num_threads);
+    int started = 0;
+    for (int k = 1; k < num_threads; ++k)
+        if (pthread_create(&th[started], NULL, worker, P) == 0) ++started;
+    worker(P);
+    for (int k = 0; k < started; ++k) pthread_join(th[k], NULL);
+    free(th);
+    return 0;
+}
+
+/* Partitioned (V2) result: out, max_logits, exp_sums, tmp_out, all float64.
+ * pair_mask (optional, [S*H]) restricts the work to selected (s, h) pairs;
+ * unselected rows of the outputs are left untouched. */
+int oracle_paged_attention_v2(
+    double *out, double *max_logits, double *exp_sums, double *tmp_out,
+    const void *query, int q_dtype,
+    const void *key_cache, const void *value_cache, int kv_dtype,
+    const int32_t *block_tables, int max_blocks_per_seq,
+    const int32_t *seq_lens, const float *alibi_slopes,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+    int max_num_partitions, float scale, float k_scale, float v_scale,
+    const uint8_t *pair_mask, int num_threads) {
+    problem_t P;
+    memset(&P, 0, sizeof(P));
+    P.query = query; P.key_cache = key_cache; P.value_cache = value_cache;
+    P.block_tables = block_tables; P.seq_lens = seq_lens; P.alibi_slopes = alibi_slopes;
+    P.q_dtype = q_dtype; P.kv_dtype = kv_dtype;
+    P.num_seqs = num_seqs; P.num_heads = num_heads; P.num_kv_heads = num_kv_heads;
+    P.head_size = head_size; P.block_size = block_size;
+    P.max_blocks_per_seq = max_blocks_per_seq; P.max_num_partitions = max_num_partitions;
+    P.scale = scale; P.k_scale = k_scale; P.v_scale = v_scale;
+    P.out = out; P.max_logits = max_logits; P.exp_sums = exp_sums; P.tmp_out = tmp_out;
+    P.pair_mask = pair_mask; P.dense = 0;
+    for (int s = 0; s < num_seqs; ++s)
+        if ((seq_lens[s] + OR_PARTITION - 1) / OR_PARTITION > max_num_partitions) return -2;
+    return run(&P, num_threads);
+}
+
+/* Unpartitioned result: one softmax over all tokens of each (s, h). */
+int oracle_dense_attention(
+    double *out,
+    const void *query, int q_dtype,
+    const void *key_cache, const void *value_cache, int kv_dtype,
+    const int32_t *block_tables, int max_blocks_per_seq,
+    const int32_t *seq_lens, const float *alibi_slopes,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+    float scale, float k_scale, float v_scale,
+    const uint8_t *pair_mask, int num_threads) {
+    problem_t P;
+    memset(&P, 0, sizeof(P));
+    P.query = query; P.key_cache = key_cache; P.value_cache = value_cache;
+    P.block_tables = block_tables; P.seq_lens = seq_lens; P.alibi_slopes = alibi_slopes;
+    P.q_dtype = q_dtype; P.kv_dtype = kv_dtype;
+    P.num_seqs = num_seqs; P.num_heads = num_heads; P.num_kv_heads = num_kv_heads;
+    P.head_size = head_size; P.block_size = block_size;
+    P.max_blocks_per_seq = max_blocks_per_seq;
+    P.scale = scale; P.k_scale = k_scale; P.v_scale = v_scale;
+    P.out = out; P.pair_mask = pair_mask; P.dense = 1;
+    return run(&P, num_threads);
+}
