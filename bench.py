@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark PagedAttention V2 decode on one MI355X.
+
+A step is one pass of the whole hot path over one batch: phase 1 (the
+per-partition kernel) and phase 2 (the log-sum-exp combine), launched through
+the C ABI on the current stream, on synthetic inputs already resident in HBM.
+
+Default workload: 4 sequences x 100000 tokens, 24 query heads over 4 kv heads
+(GQA 6), head size 256, bf16, block size 16 -- the long-context GQA decode the
+metric names.  `--config` selects one of the other workloads.
+
+Prints ONE JSON line.  `value` is KV bytes read per second (decimal GB/s);
+`roofline` reports phase 1's algorithmic bytes per launch over its mean
+duration (HIP events on the launch stream, inside the timed region) against
+MI355X's 8 TB/s HBM peak; `cpu_baseline` times the float64 CPU oracle on a
+bounded sample of the same workload and also checks those outputs against the
+GPU's.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBPS = 8000.0
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from decode_attention_paged_v2_amd import workloads as W  # noqa: E402
+import decode_attention_paged_v2_amd as pav2  # noqa: E402
+
+DESCR = {
+    "tiny": "1 seq x 1000 tokens, H=4, kv_h=4, d=64, fp32, block 16",
+    "batched_gqa": "32 seqs, L~U[512,4096], H=32, kv_h=8, d=128, fp16, block 16",
+    "long_gqa": "4 seqs x 100000 tokens, H=24, kv_h=4 (GQA 6), d=256, bf16, block 16",
+    "ragged_alibi": "256 seqs, L log-uniform [1,32768] (4 empty), H=32, kv_h=8, d=80, fp16, ALiBi, block 16",
+    "fp8_kv": "64 seqs x 16384 tokens, H=64, kv_h=8, d=128, e4m3 KV (k_scale 0.05, v_scale 0.04), bf16 q/out, block 32",
+}
+DTYPE_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
+
+def phase1_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one phase-1 launch.
+
+    K and V of every cached token once per kv head (2 * d * b_kv per
+    (token, kv head)), the query, the block-table entries the sequences use,
+    and the per-partition outputs written: tmp_output rows plus max_logits and
+    exp_sums (4 bytes each) for every (seq, head, partition) slot.
+    """
+    qb = wl.query.element_size()
+    S, H, D, P = wl.num_seqs, wl.num_heads, wl.head_size, wl.max_num_partitions
+    used_parts = sum((L + 511) // 512 for L in wl.seq_lens_host)
+    blocks = sum((L + wl.block_size - 1) // wl.block_size for L in wl.seq_lens_host)
+    return (wl.kv_bytes() + S * H * D * qb + 4 * blocks
+            + used_parts * H * D * qb + 2 * 4 * S * H * P)
+
+
+def phase2_bytes(wl) -> int:
+    """Algorithmic bytes of phase 2: read the used partition rows and stats, write output."""
+    qb = wl.query.element_size()
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_size
+    used_parts = sum((L + 511) // 512 for L in wl.seq_lens_host)
+    return used_parts * H * (D * qb + 8) + S * H * D * qb + 4 * S
+
+
+def cpu_baseline(wl, out_gpu, target_core_seconds=15.0, max_threads=16):
+    """Time the oracle on whole (seq, kv head) groups of the same workload."""
+    import oracle
+    gqa = wl.num_heads // wl.num_kv_heads
+    groups = [(s, g) for s in range(wl.num_seqs) for g in range(wl.num_kv_heads)
+              if wl.seq_lens_host[s] > 0]
+    rng = np.random.default_rng(0)
+    rng.shuffle(groups)
+    # calibrate on one head, then take enough groups for ~target core-seconds
+    s0, g0 = groups[0]
+    host = wl.to("cpu")
+    kw = dict(num_kv_heads=wl.num_kv_heads, scale=wl.scale, block_size=wl.block_size,
+              max_num_partitions=wl.max_num_partitions, q_dtype=oracle.dtype_code(wl.q_dtype),
+              kv_dtype=oracle.dtype_code(wl.kv_dtype), alibi_slopes=host.alibi_slopes,
+              k_scale=wl.k_scale, v_scale=wl.v_scale)
+    args = (host.query, host.key_cache, host.value_cache, host.block_tables, host.seq_lens)
+    t0 = time.perf_counter()
+    oracle.paged_attention_v2(*args, pairs=[(s0, g0 * gqa)], threads=1, **kw)
+    per_head = max(1e-3, time.perf_counter() - t0)
+    n_groups = int(max(1, min(len(groups), round(target_core_seconds / (per_head * gqa)))))
+    sample = groups[:n_groups]
+    pairs = [(s, g * gqa + r) for s, g in sample for r in range(gqa)]
+    threads = int(max(1, min(len(pairs), os.cpu_count() or 1, max_threads)))
+    t0 = time.perf_counter()
+    r = oracle.paged_attention_v2(*args, pairs=pairs, threads=threads, **kw)
+    dt = time.perf_counter() - t0
+    kvb = W.elem_size(wl.kv_dtype)
+    bytes_ = sum(wl.seq_lens_host[s] * 2 * wl.head_size * kvb for s, g in sample)
+    toks = sum(wl.seq_lens_host[s] for s, g in sample) * gqa
+    err = 0.0
+    for s, h in pairs:
+        ref = torch.from_numpy(r["out"][s, h]).to(wl.q_dtype).double()
+        err = max(err, float((out_gpu[s, h].double() - ref).abs().max()))
+    return {
+        "value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": (f"{n_groups} of {len(groups)} (seq, kv head) groups = {len(pairs)} query heads, "
+                   f"{bytes_ / 1e6:.1f} MB of KV, float64 C oracle, {dt:.2f} s wall"),
+        "tokens_heads_per_s": round(toks / dt, 1),
+        "seconds": round(dt, 3),
+        "parity_max_abs_err_vs_gpu": err,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="long_gqa", choices=list(W.SPECS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-steps", type=int, default=10,
+                    help="extra per-step timings with a 1 GiB cache flush before each step")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; "
+                          "--gpus above 1 is not supported"}), flush=True)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pav2.load()
+    spec = W.SPECS[args.config]
+    t0 = time.time()
+    wl = W.generate(spec, device=dev, poison=False)
+    gen_s = time.time() - t0
+
+    S, H, D, P = wl.num_seqs, wl.num_heads, wl.head_size, wl.max_num_partitions
+    out = torch.empty_like(wl.query)
+    es = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    ml = torch.empty_like(es)
+    tmp = torch.empty((S, H, P, D), dtype=wl.q_dtype, device=dev)
+    a = (wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale, wl.block_tables,
+         wl.seq_lens, wl.block_size, wl.max_seq_len)
+    kw = dict(alibi_slopes=wl.alibi_slopes, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev_a=None, ev_b=None):
+        if ev_a is not None:
+            ev_a.record(stream)
+        pav2.phase1(es, ml, tmp, *a, **kw)
+        if ev_b is not None:
+            ev_b.record(stream)
+        pav2.phase2(out, es, ml, tmp, wl.seq_lens)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(*ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p1_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms_per_step = wall * 1e3 / args.steps
+
+    # cold-cache timings: flush L2 and the 256 MB MALL with a 1 GiB write first
+    cold = []
+    if args.flush_steps > 0:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for _ in range(args.flush_steps):
+            scratch.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del scratch
+
+    kv = wl.kv_bytes()
+    b1 = phase1_bytes(wl)
+    p1_mean = float(np.mean(p1_ms))
+    achieved = b1 / (p1_mean * 1e-3) / 1e9
+    value = kv / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": "decode attention KV GB/s and % of HBM peak (Qwen-style 100K ctx, GQA 6)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[wl.q_dtype] + ("" if wl.kv_dtype == wl.q_dtype else "+fp8_e4m3_kv"),
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {DESCR[args.config]}", "num_seqs": S,
+                   "num_heads": H, "num_kv_heads": wl.num_kv_heads, "head_size": D,
+                   "block_size": wl.block_size, "max_seq_len": wl.max_seq_len,
+                   "max_num_partitions": P, "partition_size": 512},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "tokens_heads_per_s": round(wl.tokens_heads() / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": kv,
+        "phase1_ms_mean": round(p1_mean, 5),
+        "phase1_ms_min": round(float(np.min(p1_ms)), 5),
+        "phase2_plus_gap_ms": round(ms_per_step - p1_mean, 5),
+        "cold_cache_step_ms_median": round(float(np.median(cold)), 5) if cold else None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "phase1_kernel", "algorithmic_bytes_per_launch": b1},
+        "generate_s": round(gen_s, 2),
+        "library": pav2.lib_path(),
+    }
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline(wl, out.cpu())
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

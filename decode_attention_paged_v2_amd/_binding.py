@@ -1,0 +1,229 @@
+"""ctypes binding of libpav2.so: argument marshalling only.
+
+Every computation runs in the library's HIP kernels; nothing here computes
+attention, and there is no CPU fallback: if the library cannot be loaded the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from . import build as _build
+
+F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+PARTITION_SIZE = 512
+
+_lock = threading.Lock()
+_lib = None
+
+
+class Pav2Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pav2 status {status}: {message}")
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "phase1_workgroups", "phase1_threads", "phase1_lds_bytes", "head_groups",
+        "waves_per_partition", "phase2_workgroups", "phase2_threads", "phase2_lds_bytes")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def load():
+    """Load libpav2.so (building it first only if no library exists)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        attn = [P, P, P, P, P, P, P, I, F, P, P, I, I, P, I, F, F, I, I, I, I, I, I, I, P]
+        L.pav2_paged_attention_v2.argtypes = attn
+        L.pav2_paged_attention_v2.restype = I
+        L.pav2_phase1.argtypes = attn[1:]
+        L.pav2_phase1.restype = I
+        L.pav2_phase2.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+        L.pav2_phase2.restype = I
+        L.pav2_plan.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(Plan)]
+        L.pav2_plan.restype = I
+        L.pav2_decode_kv.argtypes = [P, P, ctypes.c_int64, I, I, P]
+        L.pav2_decode_kv.restype = I
+        L.pav2_max_num_partitions.argtypes = [I]
+        L.pav2_max_num_partitions.restype = I
+        L.pav2_last_error.argtypes = []
+        L.pav2_last_error.restype = ctypes.c_char_p
+        L.pav2_version.argtypes = []
+        L.pav2_version.restype = I
+        _lib = L
+        return L
+
+
+def last_error() -> str:
+    return load().pav2_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise Pav2Error(rc, last_error())
+
+
+def version() -> int:
+    return load().pav2_version()
+
+
+def max_num_partitions(max_seq_len: int) -> int:
+    return load().pav2_max_num_partitions(int(max_seq_len))
+
+
+# ---- torch marshalling ------------------------------------------------------
+
+def _dtype_code(t, kv_cache_dtype: str = "auto") -> int:
+    import torch
+    if kv_cache_dtype not in ("auto", None):
+        if kv_cache_dtype in ("fp8", "fp8_e4m3"):
+            return FP8_E4M3
+        raise ValueError(f"unsupported kv_cache_dtype {kv_cache_dtype!r}")
+    table = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
+             torch.float8_e4m3fn: FP8_E4M3}
+    if t.dtype not in table:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return table[t.dtype]
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (this library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _i32(t, name):
+    import torch
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32")
+    return _dev(t, name)
+
+
+def _common(query, key_cache, value_cache, num_kv_heads, block_tables, seq_lens, block_size,
+            kv_cache_dtype, alibi_slopes):
+    S, H, D = (int(v) for v in query.shape)
+    if key_cache.dim() != 5 or value_cache.dim() != 4:
+        raise ValueError("key_cache must be 5-D and value_cache 4-D")
+    if int(key_cache.shape[1]) != int(num_kv_heads) or int(value_cache.shape[3]) != int(block_size):
+        raise ValueError("cache shapes disagree with num_kv_heads / block_size")
+    if alibi_slopes is not None:
+        import torch
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != H:
+            raise ValueError("alibi_slopes must be float32 [num_heads]")
+    kvdt = _dtype_code(key_cache, kv_cache_dtype)
+    return S, H, D, kvdt
+
+
+def paged_attention_v2(output, exp_sums, max_logits, tmp_output, query, key_cache, value_cache,
+                       num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                       alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
+                       stream=None) -> None:
+    """The pages' V2 op: fills output, exp_sums, max_logits, tmp_output in place."""
+    L = load()
+    S, H, D, kvdt = _common(query, key_cache, value_cache, num_kv_heads, block_tables, seq_lens,
+                            block_size, kv_cache_dtype, alibi_slopes)
+    rc = L.pav2_paged_attention_v2(
+        _dev(output, "output"), _dev(exp_sums, "exp_sums"), _dev(max_logits, "max_logits"),
+        _dev(tmp_output, "tmp_output"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), int(num_kv_heads), float(scale),
+        _i32(block_tables, "block_tables"), _i32(seq_lens, "seq_lens"), int(block_size),
+        int(max_seq_len), _dev(alibi_slopes, "alibi_slopes"), kvdt, float(k_scale), float(v_scale),
+        S, H, D, int(key_cache.shape[0]), int(block_tables.shape[1]), int(tmp_output.shape[2]),
+        _dtype_code(query), _stream(query, stream))
+    _check(rc)
+
+
+def phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, num_kv_heads, scale,
+           block_tables, seq_lens, block_size, max_seq_len, alibi_slopes=None,
+           kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    L = load()
+    S, H, D, kvdt = _common(query, key_cache, value_cache, num_kv_heads, block_tables, seq_lens,
+                            block_size, kv_cache_dtype, alibi_slopes)
+    rc = L.pav2_phase1(
+        _dev(exp_sums, "exp_sums"), _dev(max_logits, "max_logits"), _dev(tmp_output, "tmp_output"),
+        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        int(num_kv_heads), float(scale), _i32(block_tables, "block_tables"),
+        _i32(seq_lens, "seq_lens"), int(block_size), int(max_seq_len),
+        _dev(alibi_slopes, "alibi_slopes"), kvdt, float(k_scale), float(v_scale),
+        S, H, D, int(key_cache.shape[0]), int(block_tables.shape[1]), int(tmp_output.shape[2]),
+        _dtype_code(query), _stream(query, stream))
+    _check(rc)
+
+
+def phase2(output, exp_sums, max_logits, tmp_output, seq_lens, stream=None) -> None:
+    L = load()
+    S, H, D = (int(v) for v in output.shape)
+    rc = L.pav2_phase2(
+        _dev(output, "output"), _dev(exp_sums, "exp_sums"), _dev(max_logits, "max_logits"),
+        _dev(tmp_output, "tmp_output"), _i32(seq_lens, "seq_lens"), S, H, D,
+        int(tmp_output.shape[2]), _dtype_code(output), _stream(output, stream))
+    _check(rc)
+
+
+def plan(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_num_partitions,
+         query_dtype: int, kv_cache_dtype: int) -> dict:
+    pl = Plan()
+    rc = load().pav2_plan(int(num_seqs), int(num_heads), int(num_kv_heads), int(head_size),
+                          int(block_size), int(max_num_partitions), int(query_dtype),
+                          int(kv_cache_dtype), ctypes.byref(pl))
+    _check(rc)
+    return pl.as_dict()
+
+
+def decode_kv(src, compute_dtype=None, stream=None):
+    """Widen a device tensor of KV-cache elements to float32 with the kernels' converters."""
+    import torch
+    kvdt = _dtype_code(src)
+    via = kvdt if compute_dtype is None else _dtype_code(torch.empty(0, dtype=compute_dtype))
+    dst = torch.empty(src.numel(), dtype=torch.float32, device=src.device)
+    rc = load().pav2_decode_kv(_dev(src, "src"), _dev(dst, "dst"), src.numel(), kvdt, via,
+                               _stream(src, stream))
+    _check(rc)
+    return dst.view(src.shape)
+
+
+def decode(query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, scale,
+           block_size, max_seq_len, alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0,
+           v_scale=1.0, stream=None):
+    """Allocate the outputs and partition buffers (torch) and run both phases.
+
+    Returns (output, exp_sums, max_logits, tmp_output).
+    """
+    import torch
+    S, H, D = (int(v) for v in query.shape)
+    P = max(1, max_num_partitions(max_seq_len))
+    dev = query.device
+    output = torch.empty_like(query)
+    exp_sums = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    max_logits = torch.empty_like(exp_sums)
+    tmp_output = torch.empty((S, H, P, D), dtype=query.dtype, device=dev)
+    paged_attention_v2(output, exp_sums, max_logits, tmp_output, query, key_cache, value_cache,
+                       num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                       alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
+    return output, exp_sums, max_logits, tmp_output

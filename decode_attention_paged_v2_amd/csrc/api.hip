@@ -1,0 +1,307 @@
+// C ABI of the PagedAttention V2 decode library: argument validation, the
+// launch planner, and the two stream-ordered launches.  No host
+// synchronisation, no device reads on the host, no allocation.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/pav2.h"
+#include "pav2_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int elem_bytes(int dt) {
+    switch (dt) {
+    case PAV2_F32: return 4;
+    case PAV2_F16: return 2;
+    case PAV2_BF16: return 2;
+    case PAV2_FP8_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+const char *dt_name(int dt) {
+    switch (dt) {
+    case PAV2_F32: return "f32";
+    case PAV2_F16: return "f16";
+    case PAV2_BF16: return "bf16";
+    case PAV2_FP8_E4M3: return "fp8_e4m3";
+    default: return "?";
+    }
+}
+
+bool supported_head_size(int d) {
+    // the head sizes the pages' backend lists as supported
+    static const int kSizes[] = {64, 80, 96, 112, 120, 128, 192, 256};
+    for (int v : kSizes)
+        if (v == d) return true;
+    return false;
+}
+
+int ilog2_exact(int v) {
+    if (v <= 0 || (v & (v - 1))) return -1;
+    int r = 0;
+    while ((1 << r) < v) ++r;
+    return r;
+}
+
+struct Shape {
+    int num_seqs, num_heads, num_kv_heads, head_size, block_size;
+    int num_blocks, max_blocks_per_seq, max_num_partitions, max_seq_len;
+    int qdt, kvdt;
+};
+
+// Shape/dtype checks shared by phase 1 and the full call.
+int check_shape(const Shape &s) {
+    if (s.num_seqs < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", s.num_seqs);
+    if (s.num_heads <= 0 || s.num_kv_heads <= 0)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "num_heads (%d) and num_kv_heads (%d) must be > 0",
+                    s.num_heads, s.num_kv_heads);
+    if (s.num_heads % s.num_kv_heads)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "num_heads (%d) is not a multiple of num_kv_heads (%d)",
+                    s.num_heads, s.num_kv_heads);
+    if (elem_bytes(s.qdt) == 0 || s.qdt == PAV2_FP8_E4M3)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "query dtype must be f32, f16 or bf16 (got %d)", s.qdt);
+    if (elem_bytes(s.kvdt) == 0)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "unknown kv_cache_dtype %d", s.kvdt);
+    if (!supported_head_size(s.head_size))
+        return fail(PAV2_ERR_UNSUPPORTED, "head_size %d is not one of 64, 80, 96, 112, 120, 128, 192, 256",
+                    s.head_size);
+    const int x = 16 / elem_bytes(s.kvdt);
+    if (s.head_size % x)
+        return fail(PAV2_ERR_UNSUPPORTED, "head_size %d is not a multiple of x = %d for kv dtype %s",
+                    s.head_size, x, dt_name(s.kvdt));
+    if (s.kvdt != s.qdt && s.kvdt != PAV2_FP8_E4M3)
+        return fail(PAV2_ERR_UNSUPPORTED, "query dtype %s with kv dtype %s is not supported",
+                    dt_name(s.qdt), dt_name(s.kvdt));
+    if (ilog2_exact(s.block_size) < 2 || PAV2_PARTITION_SIZE % s.block_size)
+        return fail(PAV2_ERR_INVALID_ARGUMENT,
+                    "block_size %d must be a power of two in [4, 512] dividing the 512-token partition",
+                    s.block_size);
+    if (s.num_blocks <= 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
+    if (s.max_seq_len < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 0");
+    const int need = (s.max_seq_len + PAV2_PARTITION_SIZE - 1) / PAV2_PARTITION_SIZE;
+    if (s.max_num_partitions < need || s.max_num_partitions < 1)
+        return fail(PAV2_ERR_INVALID_ARGUMENT,
+                    "max_num_partitions %d < ceil(max_seq_len / 512) = %d", s.max_num_partitions, need);
+    if (s.max_num_partitions > pav2::kMaxPartitions)
+        return fail(PAV2_ERR_UNSUPPORTED, "max_num_partitions %d exceeds %d", s.max_num_partitions,
+                    pav2::kMaxPartitions);
+    const int64_t blocks_need = ((int64_t)s.max_seq_len + s.block_size - 1) / s.block_size;
+    if (s.max_blocks_per_seq < blocks_need || s.max_blocks_per_seq < 1)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "max_blocks_per_seq %d < ceil(max_seq_len / block_size) = %lld",
+                    s.max_blocks_per_seq, (long long)blocks_need);
+    const int64_t work = (int64_t)s.num_seqs * s.num_heads * s.max_num_partitions;
+    if (work > (int64_t)1 << 30)
+        return fail(PAV2_ERR_UNSUPPORTED, "num_seqs * num_heads * max_num_partitions = %lld is too large",
+                    (long long)work);
+    return PAV2_OK;
+}
+
+void make_plan(const Shape &s, pav2_plan_t *pl) {
+    const int gqa = s.num_heads / s.num_kv_heads;
+    const int hg = (gqa + pav2::kMaxHeadsPerGroup - 1) / pav2::kMaxHeadsPerGroup;
+    const int bs_log2 = ilog2_exact(s.block_size);
+    const int64_t work = (int64_t)s.num_seqs * s.num_kv_heads * hg * s.max_num_partitions;
+    pl->head_groups = hg;
+    pl->waves_per_partition = pav2::kPhase1Waves;
+    pl->phase1_workgroups = (int)((work + 7) / 8 * 8);
+    pl->phase1_threads = pav2::kPhase1Waves * 64;
+    pl->phase1_lds_bytes = pav2::phase1_lds_bytes(gqa, s.head_size, pav2::kPhase1Waves, bs_log2);
+    pl->phase2_workgroups = s.num_seqs * s.num_heads;
+    pl->phase2_threads = pav2::kPhase2Threads;
+    pl->phase2_lds_bytes = pav2::phase2_lds_bytes(s.max_num_partitions, s.head_size, s.qdt);
+}
+
+int launch_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return PAV2_OK;
+    if (e == hipErrorInvalidValue)
+        return fail(PAV2_ERR_UNSUPPORTED, "%s: no kernel variant for this combination", what);
+    return fail(PAV2_ERR_LAUNCH, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+int run_phase1(float *exp_sums, float *max_logits, void *tmp_output, const void *query,
+               const void *key_cache, const void *value_cache, float scale,
+               const int32_t *block_tables, const int32_t *seq_lens, const float *alibi_slopes,
+               float k_scale, float v_scale, const Shape &sh, hipStream_t stream) {
+    pav2_plan_t pl;
+    make_plan(sh, &pl);
+    pav2::Phase1Params p;
+    p.tmp_out = tmp_output;
+    p.exp_sums = exp_sums;
+    p.max_logits = max_logits;
+    p.query = query;
+    p.key_cache = static_cast<const uint8_t *>(key_cache);
+    p.value_cache = static_cast<const uint8_t *>(value_cache);
+    p.block_tables = block_tables;
+    p.seq_lens = seq_lens;
+    p.alibi = alibi_slopes;
+    p.num_seqs = sh.num_seqs;
+    p.num_heads = sh.num_heads;
+    p.num_kv_heads = sh.num_kv_heads;
+    p.gqa = sh.num_heads / sh.num_kv_heads;
+    p.head_groups = pl.head_groups;
+    p.bs_log2 = ilog2_exact(sh.block_size);
+    p.max_blocks_per_seq = sh.max_blocks_per_seq;
+    p.max_num_partitions = sh.max_num_partitions;
+    p.num_work = sh.num_seqs * sh.num_kv_heads * pl.head_groups * sh.max_num_partitions;
+    p.head_stride = (int64_t)sh.head_size * sh.block_size * elem_bytes(sh.kvdt);
+    p.blk_stride = p.head_stride * sh.num_kv_heads;
+    p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+    p.v_scale = v_scale;
+    return launch_status(pav2::launch_phase1(p, sh.qdt, sh.kvdt, sh.head_size, pl.waves_per_partition,
+                                             pl.phase1_lds_bytes, stream),
+                         "phase 1");
+}
+
+int run_phase2(void *output, const float *exp_sums, const float *max_logits, const void *tmp_output,
+               const int32_t *seq_lens, int num_seqs, int num_heads, int head_size,
+               int max_num_partitions, int odt, hipStream_t stream) {
+    pav2::Phase2Params p;
+    p.out = output;
+    p.exp_sums = exp_sums;
+    p.max_logits = max_logits;
+    p.tmp_out = tmp_output;
+    p.seq_lens = seq_lens;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.max_num_partitions = max_num_partitions;
+    const int lds = pav2::phase2_lds_bytes(max_num_partitions, head_size, odt);
+    return launch_status(pav2::launch_phase2(p, odt, head_size, pav2::kPhase2Threads, lds, stream),
+                         "phase 2");
+}
+
+int check_phase1_args(float *exp_sums, float *max_logits, void *tmp_output, const void *query,
+                      const void *key_cache, const void *value_cache, const int32_t *block_tables,
+                      const int32_t *seq_lens, float scale, float k_scale, float v_scale) {
+    if (!exp_sums || !max_logits || !tmp_output || !query || !key_cache || !value_cache ||
+        !block_tables || !seq_lens)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (!isfinite(scale) || !isfinite(k_scale) || !isfinite(v_scale))
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "scale, k_scale and v_scale must be finite");
+    return PAV2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pav2_phase1(float *exp_sums, float *max_logits, void *tmp_output, const void *query,
+                const void *key_cache, const void *value_cache, int num_kv_heads, float scale,
+                const int32_t *block_tables, const int32_t *seq_lens, int block_size,
+                int max_seq_len, const float *alibi_slopes, pav2_dtype_t kv_cache_dtype,
+                float k_scale, float v_scale, int num_seqs, int num_heads, int head_size,
+                int num_blocks, int max_blocks_per_seq, int max_num_partitions,
+                pav2_dtype_t query_dtype, pav2_stream_t stream) {
+    g_err[0] = 0;
+    Shape sh{num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks,
+             max_blocks_per_seq, max_num_partitions, max_seq_len, (int)query_dtype, (int)kv_cache_dtype};
+    int rc = check_shape(sh);
+    if (rc) return rc;
+    if (num_seqs == 0) return PAV2_OK;
+    rc = check_phase1_args(exp_sums, max_logits, tmp_output, query, key_cache, value_cache,
+                           block_tables, seq_lens, scale, k_scale, v_scale);
+    if (rc) return rc;
+    return run_phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, scale,
+                      block_tables, seq_lens, alibi_slopes, k_scale, v_scale, sh,
+                      static_cast<hipStream_t>(stream));
+}
+
+int pav2_phase2(void *output, const float *exp_sums, const float *max_logits,
+                const void *tmp_output, const int32_t *seq_lens, int num_seqs, int num_heads,
+                int head_size, int max_num_partitions, pav2_dtype_t out_dtype,
+                pav2_stream_t stream) {
+    g_err[0] = 0;
+    if (num_seqs < 0 || num_heads <= 0)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 and num_heads > 0");
+    if (out_dtype != PAV2_F32 && out_dtype != PAV2_F16 && out_dtype != PAV2_BF16)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "output dtype must be f32, f16 or bf16");
+    if (!supported_head_size(head_size))
+        return fail(PAV2_ERR_UNSUPPORTED, "head_size %d is not supported", head_size);
+    if (max_num_partitions < 1 || max_num_partitions > pav2::kMaxPartitions)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "max_num_partitions %d out of [1, %d]", max_num_partitions,
+                    pav2::kMaxPartitions);
+    if (num_seqs == 0) return PAV2_OK;
+    if (!output || !exp_sums || !max_logits || !tmp_output || !seq_lens)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    return run_phase2(output, exp_sums, max_logits, tmp_output, seq_lens, num_seqs, num_heads, head_size,
+                      max_num_partitions, (int)out_dtype, static_cast<hipStream_t>(stream));
+}
+
+int pav2_paged_attention_v2(void *output, float *exp_sums, float *max_logits, void *tmp_output,
+                            const void *query, const void *key_cache, const void *value_cache,
+                            int num_kv_heads, float scale, const int32_t *block_tables,
+                            const int32_t *seq_lens, int block_size, int max_seq_len,
+                            const float *alibi_slopes, pav2_dtype_t kv_cache_dtype, float k_scale,
+                            float v_scale, int num_seqs, int num_heads, int head_size,
+                            int num_blocks, int max_blocks_per_seq, int max_num_partitions,
+                            pav2_dtype_t query_dtype, pav2_stream_t stream) {
+    g_err[0] = 0;
+    Shape sh{num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks,
+             max_blocks_per_seq, max_num_partitions, max_seq_len, (int)query_dtype, (int)kv_cache_dtype};
+    int rc = check_shape(sh);
+    if (rc) return rc;
+    if (num_seqs == 0) return PAV2_OK;
+    if (!output) return fail(PAV2_ERR_INVALID_ARGUMENT, "output is NULL");
+    rc = check_phase1_args(exp_sums, max_logits, tmp_output, query, key_cache, value_cache,
+                           block_tables, seq_lens, scale, k_scale, v_scale);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = run_phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, scale,
+                    block_tables, seq_lens, alibi_slopes, k_scale, v_scale, sh, st);
+    if (rc) return rc;
+    return run_phase2(output, exp_sums, max_logits, tmp_output, seq_lens, num_seqs, num_heads,
+                      head_size, max_num_partitions, (int)query_dtype, st);
+}
+
+int pav2_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+              int max_num_partitions, pav2_dtype_t query_dtype, pav2_dtype_t kv_cache_dtype,
+              pav2_plan_t *plan) {
+    g_err[0] = 0;
+    if (!plan) return fail(PAV2_ERR_INVALID_ARGUMENT, "plan is NULL");
+    const int max_seq_len = max_num_partitions * PAV2_PARTITION_SIZE;
+    Shape sh{num_seqs, num_heads, num_kv_heads, head_size, block_size, 1,
+             (max_seq_len + (block_size > 0 ? block_size : 1) - 1) / (block_size > 0 ? block_size : 1),
+             max_num_partitions, max_seq_len, (int)query_dtype, (int)kv_cache_dtype};
+    int rc = check_shape(sh);
+    if (rc) return rc;
+    make_plan(sh, plan);
+    return PAV2_OK;
+}
+
+int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype,
+                   pav2_dtype_t compute_dtype, pav2_stream_t stream) {
+    g_err[0] = 0;
+    if (n < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "n must be >= 0");
+    if (n == 0) return PAV2_OK;
+    if (!src || !dst) return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (elem_bytes(kv_dtype) == 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "unknown kv dtype %d", kv_dtype);
+    if (kv_dtype != PAV2_FP8_E4M3) compute_dtype = kv_dtype;
+    if (compute_dtype != PAV2_F32 && compute_dtype != PAV2_F16 && compute_dtype != PAV2_BF16)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "compute dtype must be f32, f16 or bf16");
+    return launch_status(pav2::launch_decode_kv(src, dst, n, (int)kv_dtype, (int)compute_dtype,
+                                                static_cast<hipStream_t>(stream)),
+                         "decode_kv");
+}
+
+int pav2_max_num_partitions(int max_seq_len) {
+    if (max_seq_len <= 0) return 0;
+    return (int)(((int64_t)max_seq_len + PAV2_PARTITION_SIZE - 1) / PAV2_PARTITION_SIZE);
+}
+
+const char *pav2_last_error(void) { return g_err; }
+
+int pav2_version(void) { return PAV2_VERSION; }
+
+}  // extern "C"

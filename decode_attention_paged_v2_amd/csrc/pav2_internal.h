@@ -1,0 +1,99 @@
+// Internal declarations shared by the PagedAttention V2 kernels and the C ABI.
+// gfx950 (CDNA4) only: 64-lane wavefronts, MFMA 16x16xK tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pav2 {
+
+constexpr int kPartition = 512;                 // tokens per partition
+constexpr int kTile = 16;                       // tokens per MFMA tile
+constexpr int kTilesPerPartition = kPartition / kTile;
+constexpr int kMaxHeadsPerGroup = 16;           // query heads per MFMA N-tile
+constexpr int kMaxPartitions = 16384;
+
+enum Dtype { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Scalar reinterpretation goes through these by-value helpers: with this
+// compiler, __builtin_bit_cast applied directly to an element of an
+// ext_vector_type lvalue (v[i]) reinterprets the vector's first element
+// whatever i is, so elements are always copied out as values first.
+__device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ uint32_t as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t x) { return __builtin_bit_cast(f16x2, x); }
+
+struct Phase1Params {
+    void *tmp_out;                 // [S, H, maxP, D] out dtype
+    float *exp_sums;               // [S, H, maxP]
+    float *max_logits;             // [S, H, maxP]
+    const void *query;             // [S, H, D]
+    const uint8_t *key_cache;      // [NB, KVH, D/x, BS, x]
+    const uint8_t *value_cache;    // [NB, KVH, D, BS]
+    const int32_t *block_tables;   // [S, MBPS]
+    const int32_t *seq_lens;       // [S]
+    const float *alibi;            // [H] or null
+    int num_seqs, num_heads, num_kv_heads;
+    int gqa;                       // num_heads / num_kv_heads
+    int head_groups;               // ceil(gqa / 16)
+    int bs_log2;                   // log2(block_size)
+    int max_blocks_per_seq;
+    int max_num_partitions;
+    int num_work;                  // S * KVH * head_groups * maxP
+    int64_t blk_stride;            // bytes per physical block (all kv heads)
+    int64_t head_stride;           // bytes per (block, kv head)
+    float scale_log2;              // scale * k_scale * log2(e)
+    float v_scale;
+};
+
+struct Phase2Params {
+    void *out;                     // [S, H, D]
+    const float *exp_sums;
+    const float *max_logits;
+    const void *tmp_out;
+    const int32_t *seq_lens;
+    int num_seqs, num_heads, max_num_partitions;
+};
+
+// Host-side launchers (one per translation unit that defines the kernels).
+// Return hipSuccess, or hipErrorInvalidValue for an unsupported combination.
+hipError_t launch_phase1(const Phase1Params &p, int qdt, int kvdt, int head_size,
+                         int waves, int lds_bytes, hipStream_t stream);
+hipError_t launch_phase2(const Phase2Params &p, int odt, int head_size, int threads,
+                         int lds_bytes, hipStream_t stream);
+hipError_t launch_decode_kv(const void *src, float *dst, int64_t n, int dtype, int via,
+                            hipStream_t stream);
+
+// Phase-1 workgroup shape.
+constexpr int kPhase1Waves = 4;
+constexpr int kPhase2Threads = 256;
+
+inline int phase1_lds_bytes(int gqa, int head_size, int waves, int bs_log2) {
+    int heads = gqa < kMaxHeadsPerGroup ? gqa : kMaxHeadsPerGroup;
+    int d16 = (head_size + 15) / 16 * 16;
+    int table = (kPartition >> bs_log2) * 4;
+    return waves * heads * (d16 + 4) * 4      // per-wave partial outputs
+           + 3 * waves * kMaxHeadsPerGroup * 4 // per-wave max and sums
+           + table;                            // the partition's block-table slice
+}
+
+inline int phase2_vec(int odt) { return odt == F32 ? 4 : 8; }
+
+inline int phase2_lds_bytes(int max_num_partitions, int head_size, int odt) {
+    int vec = phase2_vec(odt);
+    int rows = kPhase2Threads / (head_size / vec);
+    return max_num_partitions * 4 + rows * head_size * 4 + 64 * 4;
+}
+
+}  // namespace pav2

@@ -1,0 +1,551 @@
+// Phase 1 of PagedAttention V2 decode on gfx950: one workgroup per
+// (sequence, kv head, group of <= 16 query heads, 512-token partition).
+//
+// What it computes (page "paged_attention_v2_pytorch.py", the per-sequence
+// body of paged_attention_v2_pytorch; page "paged_attention_v2_triton.py",
+// _paged_attn_v2_partition_kernel for the per-partition decomposition):
+// for every query head h of the group and the partition's tokens t,
+//   z_t = scale * k_scale * (q_h . K_t) + alibi_h * t,
+//   m = max z_t, l = sum exp(z_t - m), o = v_scale * sum exp(z_t - m) V_t / l,
+// stored as max_logits, exp_sums and tmp_output.  A partition that starts at
+// or past the sequence end only stores max_logits = -inf, exp_sums = 0.
+//
+// Mapping onto CDNA4:
+// * Scores are S^T = K Q^T on 16x16 MFMA tiles: 16 tokens (M) x 16 query
+//   heads (N), contracting over the head dimension.  In the key-cache layout
+//   [.., d/x, block_size, x] one 16-byte vector is x consecutive head-dim
+//   elements of one token, which is exactly one lane's A-operand slice for a
+//   16x16x32 (16-bit) step, so K goes from HBM straight into MFMA registers:
+//   per step the wavefront reads 64 such vectors (1 KB, contiguous when the
+//   block size is 16).
+// * The S^T accumulator leaves each lane holding 4 consecutive tokens of one
+//   head, which is exactly the B-operand slice of a 16x16x16 step of
+//   O^T = V^T P^T; V^T's A-operand slice (4 consecutive tokens of one head-dim
+//   row) is one 8-byte load from the value-cache layout [.., d, block_size].
+//   No LDS traffic or lane shuffles sit between the two products.
+// * The query heads that share a kv head (GQA) are the N dimension, so each
+//   K/V byte is read once per kv head, not once per query head.
+// * Two passes per wavefront: all scores of its tiles first (registers), then
+//   one max, then exp and P V with no running rescale.  The wavefronts of a
+//   workgroup split the partition's 16-token tiles round-robin and merge their
+//   (max, sum, output) once through LDS at the end.
+// * Loads run PF tiles ahead of the MFMAs (K, then V, as one stream), so V
+//   loads are in flight while the score max is reduced.
+// * fp8 e4m3 caches are widened in registers by the hardware converters to
+//   the query's 16-bit type (exact) or to f32; k_scale folds into the score
+//   scale and v_scale into the final division.
+// * P is split into two 16-bit parts (hi + lo) that enter one 16x16x32 MFMA
+//   against the V slice duplicated, so the weights keep ~16 significant bits
+//   at the MFMA count of a single 16x16x16 product.
+// * exp2 with log2(e) folded into the score scale; ALiBi is added relative to
+//   the partition's last token (bias slope * (t - last), |t - last| < 512, so
+//   scores stay small where they matter), and the stored max_logits are
+//   shifted back to the absolute frame the pages use.
+#include <math.h>
+
+#include "pav2_internal.h"
+
+namespace pav2 {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- 16-bit packing / fp8 widening (gfx950 converters) --------------------
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (DT == BF16) {
+        bf16x2 v;
+        v[0] = (__bf16)a;
+        v[1] = (__bf16)b;
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        f16x2 v;
+        v[0] = (_Float16)a;
+        v[1] = (_Float16)b;
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float unpack_lo(uint32_t w) {
+    if constexpr (DT == BF16) return as_f32(w << 16);
+    else return (float)as_f16x2(w)[0];
+}
+
+template <int DT>
+__device__ __forceinline__ float unpack_hi(uint32_t w) {
+    if constexpr (DT == BF16) return as_f32(w & 0xffff0000u);
+    else return (float)as_f16x2(w)[1];
+}
+
+// Bytes 0,1 (HI = false) or 2,3 (HI = true) of w, e4m3 -> two 16-bit values.
+template <int DT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w) {
+    if constexpr (DT == BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+// ---- MFMA wrappers ----------------------------------------------------------
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (DT == BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_k4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_groups(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Compile-time shape of one (query dtype, kv dtype, head size) variant.
+template <int QDT, int KVDT, int D>
+struct Shape {
+    static constexpr bool kF32 = (QDT == F32);          // f32 MFMA family
+    static constexpr int kKvBytes = KVDT == F32 ? 4 : (KVDT == FP8 ? 1 : 2);
+    static constexpr int kX = 16 / kKvBytes;            // elements per 16-byte K vector
+    static constexpr int kChunks = D / kX;              // K vectors per token
+    static constexpr int kKLoads = (kChunks + 3) / 4;   // K vectors per lane per tile
+    static constexpr int kDTiles = (D + 15) / 16;       // 16-row head-dim tiles for P V
+    static constexpr int kD16 = kDTiles * 16;
+    // V^T slice of one lane per head-dim tile: 4 tokens of one row.
+    static constexpr int kVWords = (4 * kKvBytes + 3) / 4;   // 32-bit words per slice
+};
+
+template <int N>
+struct Words {
+    uint32_t w[N];
+};
+
+template <int QDT, int KVDT, int D, int WAVES, int PF>
+__global__ void __launch_bounds__(WAVES * 64)
+phase1_kernel(const Phase1Params P) {
+    using S = Shape<QDT, KVDT, D>;
+    constexpr int TPW = kTilesPerPartition / WAVES;   // tiles per wavefront
+    constexpr int NKL = S::kKLoads;
+    constexpr int NDT = S::kDTiles;
+    constexpr int X = S::kX;
+    constexpr int KVB = S::kKvBytes;
+    constexpr int QB = QDT == F32 ? 4 : 2;            // query element bytes
+
+    extern __shared__ __align__(16) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int col = lane & 15;   // token row (K^T loads), head column (outputs), head-dim row (V^T loads)
+    const int grp = lane >> 4;   // 4-element slice index within the MFMA operand
+
+    // Work item; consecutive items land on the same XCD (blockIdx.x % 8).
+    const int nblk = gridDim.x;
+    int work = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    if (work >= P.num_work) return;
+    const int hg = work % P.head_groups;
+    work /= P.head_groups;
+    const int g = work % P.num_kv_heads;
+    work /= P.num_kv_heads;
+    const int s = work % P.num_seqs;
+    const int p = work / P.num_seqs;
+
+    const int maxP = P.max_num_partitions;
+    const int L = P.seq_lens[s];
+    const int start = p * kPartition;
+    const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
+    const int nh = min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
+
+    if (start >= L) {   // unused partition slot
+        if (tid < nh) {
+            const int64_t i = ((int64_t)s * P.num_heads + h0 + tid) * maxP + p;
+            P.max_logits[i] = -INFINITY;
+            P.exp_sums[i] = 0.0f;
+        }
+        return;
+    }
+    const int n_tok = min(kPartition, L - start);
+    const int last = start + n_tok - 1;   // ALiBi reference position: the partition's last token
+    const int ntiles = (n_tok + kTile - 1) / kTile;
+
+    // LDS: per-wave partial outputs, per-wave max/sum, block-table slice.
+    const int heads_alloc = min(P.gqa, kMaxHeadsPerGroup);
+    float *s_o = reinterpret_cast<float *>(smem);
+    float *s_m = s_o + WAVES * heads_alloc * (S::kD16 + 4);
+    float *s_l = s_m + WAVES * kMaxHeadsPerGroup;
+    float *s_lr = s_l + WAVES * kMaxHeadsPerGroup;
+    int *s_bt = reinterpret_cast<int *>(s_lr + WAVES * kMaxHeadsPerGroup);
+
+    const int bs_log2 = P.bs_log2;
+    const int bs_mask = (1 << bs_log2) - 1;
+    {
+        const int n_all = kPartition >> bs_log2;
+        const int n_used = (n_tok + bs_mask) >> bs_log2;
+        const int32_t *bt = P.block_tables + (int64_t)s * P.max_blocks_per_seq + (start >> bs_log2);
+        for (int i = tid; i < n_all; i += WAVES * 64) s_bt[i] = i < n_used ? bt[i] : 0;
+    }
+
+    // Query operand (B of S^T = K Q^T): head h0 + col, head-dim slice of K vector
+    // (4u + grp), i.e. elements d = X * (4u + grp) + e.
+    const bool hvalid = col < nh;
+    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(P.query) +
+                          (((int64_t)s * P.num_heads + h0 + col) * D) * QB;
+    Words<X * QB / 4> qw[NKL];
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) {
+        const int c = 4 * u + grp;
+        const bool ok = hvalid && c < S::kChunks;
+#pragma unroll
+        for (int k = 0; k < X * QB / 16; ++k) {
+            u32x4 v = {0, 0, 0, 0};
+            if (ok) v = *reinterpret_cast<const u32x4 *>(qrow + (int64_t)c * X * QB + 16 * k);
+            qw[u].w[4 * k + 0] = v[0];
+            qw[u].w[4 * k + 1] = v[1];
+            qw[u].w[4 * k + 2] = v[2];
+            qw[u].w[4 * k + 3] = v[3];
+        }
+    }
+
+    float slope2 = 0.0f;
+    if (P.alibi != nullptr && hvalid) slope2 = P.alibi[h0 + col] * kLog2e;
+    const float scale_log2 = P.scale_log2;
+
+    __syncthreads();   // block-table slice ready
+
+    const uint8_t *kc = P.key_cache + (int64_t)g * P.head_stride;
+    const uint8_t *vc = P.value_cache + (int64_t)g * P.head_stride;
+    const int64_t blk_stride = P.blk_stride;
+
+    // Tile k of this wavefront: partition tile wv + WAVES * k, clamped to
+    // tile 0 when past the end (its tokens are then all masked).
+    auto tile_of = [&](int k) { return wv + WAVES * k; };
+    auto clamp_tile = [&](int t) { return t < ntiles ? t : 0; };
+
+    // ---- load helpers ----------------------------------------------------
+    auto load_k = [&](u32x4 (&dst)[NKL], int k) {
+        const int t = clamp_tile(tile_of(k));
+        const int o = t * kTile + col;                       // token offset in partition
+        const int64_t b = s_bt[o >> bs_log2];
+        const uint8_t *base = kc + b * blk_stride + (o & bs_mask) * 16 + (grp << (bs_log2 + 4));
+#pragma unroll
+        for (int u = 0; u < NKL; ++u) {
+            u32x4 v = {0, 0, 0, 0};
+            if (4 * u + grp < S::kChunks)
+                v = *reinterpret_cast<const u32x4 *>(base + ((int64_t)(4 * u) << (bs_log2 + 4)));
+            dst[u] = v;
+        }
+    };
+    auto load_v = [&](Words<S::kVWords> (&dst)[NDT], int k) {
+        const int t = clamp_tile(tile_of(k));
+        const int o = t * kTile + 4 * grp;                   // first of the lane's 4 tokens
+        const int64_t b = s_bt[o >> bs_log2];
+        const uint8_t *base = vc + b * blk_stride + (o & bs_mask) * KVB + (col << bs_log2) * KVB;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const uint8_t *ptr = base + ((int64_t)(16 * dt) << bs_log2) * KVB;
+            const bool ok = (D % 16 == 0) || (16 * dt + col < D);
+            if constexpr (S::kVWords == 1) {
+                dst[dt].w[0] = ok ? *reinterpret_cast<const uint32_t *>(ptr) : 0u;
+            } else if constexpr (S::kVWords == 2) {
+                u32x2 v = {0, 0};
+                if (ok) v = *reinterpret_cast<const u32x2 *>(ptr);
+                dst[dt].w[0] = v[0];
+                dst[dt].w[1] = v[1];
+            } else {
+                u32x4 v = {0, 0, 0, 0};
+                if (ok) v = *reinterpret_cast<const u32x4 *>(ptr);
+                dst[dt].w[0] = v[0];
+                dst[dt].w[1] = v[1];
+                dst[dt].w[2] = v[2];
+                dst[dt].w[3] = v[3];
+            }
+        }
+    };
+
+    // ---- S^T tile from K vectors ---------------------------------------------
+    auto qk_tile = [&](const u32x4 (&kr)[NKL]) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NKL; ++u) {
+            if constexpr (!S::kF32 && KVDT != FP8) {
+                u32x4 qv = {qw[u].w[0], qw[u].w[1], qw[u].w[2], qw[u].w[3]};
+                acc = mfma_k32<QDT>(kr[u], qv, acc);
+            } else if constexpr (!S::kF32) {   // fp8 K -> 16-bit, two steps per vector
+                u32x4 k0 = {fp8x2_to_16<QDT, false>(kr[u][0]), fp8x2_to_16<QDT, true>(kr[u][0]),
+                            fp8x2_to_16<QDT, false>(kr[u][1]), fp8x2_to_16<QDT, true>(kr[u][1])};
+                u32x4 k1 = {fp8x2_to_16<QDT, false>(kr[u][2]), fp8x2_to_16<QDT, true>(kr[u][2]),
+                            fp8x2_to_16<QDT, false>(kr[u][3]), fp8x2_to_16<QDT, true>(kr[u][3])};
+                u32x4 q0 = {qw[u].w[0], qw[u].w[1], qw[u].w[2], qw[u].w[3]};
+                u32x4 q1 = {qw[u].w[4], qw[u].w[5], qw[u].w[6], qw[u].w[7]};
+                acc = mfma_k32<QDT>(k0, q0, acc);
+                acc = mfma_k32<QDT>(k1, q1, acc);
+            } else if constexpr (KVDT == F32) {   // f32: four 16x16x4 steps per vector
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc = mfma_k4(as_f32(kr[u][e]), as_f32(qw[u].w[e]), acc);
+            } else {                              // fp8 K with f32 query
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd) {
+                    f32x2 lo = fp8x2_to_f32<false>(kr[u][wd]);
+                    f32x2 hi = fp8x2_to_f32<true>(kr[u][wd]);
+                    acc = mfma_k4(lo[0], as_f32(qw[u].w[4 * wd + 0]), acc);
+                    acc = mfma_k4(lo[1], as_f32(qw[u].w[4 * wd + 1]), acc);
+                    acc = mfma_k4(hi[0], as_f32(qw[u].w[4 * wd + 2]), acc);
+                    acc = mfma_k4(hi[1], as_f32(qw[u].w[4 * wd + 3]), acc);
+                }
+            }
+        }
+        return acc;
+    };
+
+    // ---- O^T += V^T P^T for one tile -------------------------------------------
+    f32x4 o[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto pv_tile = [&](Words<S::kVWords> (&vr)[NDT], const float (&pr)[4], u32x4 pb, int k) {
+        const int tok0 = start + tile_of(k) * kTile + 4 * grp;   // unclamped
+        const bool partial = start + tile_of(k) * kTile + kTile > L;   // wave-uniform
+        if constexpr (!S::kF32) {
+            uint32_t m0 = 0xffffffffu, m1 = 0xffffffffu;
+            if (partial) {
+                m0 = (tok0 + 0 < L ? 0x0000ffffu : 0u) | (tok0 + 1 < L ? 0xffff0000u : 0u);
+                m1 = (tok0 + 2 < L ? 0x0000ffffu : 0u) | (tok0 + 3 < L ? 0xffff0000u : 0u);
+            }
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                uint32_t a0, a1;
+                if constexpr (KVDT == FP8) {
+                    a0 = fp8x2_to_16<QDT, false>(vr[dt].w[0]);
+                    a1 = fp8x2_to_16<QDT, true>(vr[dt].w[0]);
+                } else {
+                    a0 = vr[dt].w[0];
+                    a1 = vr[dt].w[1];
+                }
+                a0 &= m0;
+                a1 &= m1;
+                // K = 32: the lane's 4 tokens twice, against P's high and low parts
+                const u32x4 a = {a0, a1, a0, a1};
+                o[dt] = mfma_k32<QDT>(a, pb, o[dt]);
+            }
+        } else {
+            bool ok[4] = {true, true, true, true};
+            if (partial) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ok[e] = tok0 + e < L;
+            }
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                float a[4];
+                if constexpr (KVDT == FP8) {
+                    f32x2 lo = fp8x2_to_f32<false>(vr[dt].w[0]);
+                    f32x2 hi = fp8x2_to_f32<true>(vr[dt].w[0]);
+                    a[0] = lo[0]; a[1] = lo[1]; a[2] = hi[0]; a[3] = hi[1];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = as_f32(vr[dt].w[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[dt] = mfma_k4(ok[e] ? a[e] : 0.0f, pr[e], o[dt]);
+            }
+        }
+    };
+
+    // ---- one stream of 2*TPW loads (K tiles, then V tiles), PF ahead --------
+    u32x4 kbuf[PF][NKL];
+    Words<S::kVWords> vbuf[PF][NDT];
+    float sc[TPW][4];
+
+    auto issue = [&](int j) {
+        if (j < TPW) load_k(kbuf[j % PF], j);
+        else if (j < 2 * TPW) load_v(vbuf[(j - TPW) % PF], j - TPW);
+    };
+
+#pragma unroll
+    for (int j = 0; j < PF; ++j) issue(j);
+
+    // Pass 1: scores.
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        f32x4 acc = qk_tile(kbuf[k % PF]);
+        issue(k + PF);
+        const int tok0 = start + tile_of(k) * kTile + 4 * grp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = tok0 + i;
+            float v = acc[i] * scale_log2 + slope2 * (float)(tok - last);
+            sc[k][i] = tok < L ? v : -INFINITY;
+        }
+    }
+
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, sc[k][i]);
+    m = wave_max(m);
+    const float mu = (m == -INFINITY) ? 0.0f : m;
+
+    // Pass 2: exp and P V.  lsum is the exact sum of the weights (stored as
+    // exp_sums); lsum_r sums the weights as rounded into the MFMA operand, so
+    // that the partition output is a true weighted mean of V rows.
+    float lsum = 0.0f, lsum_r = 0.0f;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[i] = exp2_fast(sc[k][i] - mu);
+            lsum += pr[i];
+        }
+        u32x4 pb = {0u, 0u, 0u, 0u};
+        if constexpr (!S::kF32) {
+            // P = hi + lo, both 16-bit: the pair carries ~16 significant bits.
+            const uint32_t h01 = pack2<QDT>(pr[0], pr[1]);
+            const uint32_t h23 = pack2<QDT>(pr[2], pr[3]);
+            const float r0 = pr[0] - unpack_lo<QDT>(h01), r1 = pr[1] - unpack_hi<QDT>(h01);
+            const float r2 = pr[2] - unpack_lo<QDT>(h23), r3 = pr[3] - unpack_hi<QDT>(h23);
+            const uint32_t l01 = pack2<QDT>(r0, r1);
+            const uint32_t l23 = pack2<QDT>(r2, r3);
+            pb = u32x4{h01, h23, l01, l23};
+            lsum_r += (unpack_lo<QDT>(h01) + unpack_lo<QDT>(l01)) + (unpack_hi<QDT>(h01) + unpack_hi<QDT>(l01)) +
+                      (unpack_lo<QDT>(h23) + unpack_lo<QDT>(l23)) + (unpack_hi<QDT>(h23) + unpack_hi<QDT>(l23));
+        }
+        pv_tile(vbuf[k % PF], pr, pb, k);
+        issue(TPW + k + PF);
+    }
+    lsum = wave_sum_groups(lsum);
+    if constexpr (S::kF32) lsum_r = lsum;
+    else lsum_r = wave_sum_groups(lsum_r);
+
+    // ---- merge the wavefronts through LDS ---------------------------------------
+    constexpr int RS = S::kD16 + 4;   // row stride (floats) of s_o
+    if (hvalid) {
+        if (grp == 0) {
+            s_m[wv * kMaxHeadsPerGroup + col] = m;
+            s_l[wv * kMaxHeadsPerGroup + col] = lsum;
+            s_lr[wv * kMaxHeadsPerGroup + col] = lsum_r;
+        }
+        float *dst = s_o + (wv * heads_alloc + col) * RS;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int row = 16 * dt + 4 * grp;
+            if (row < D) *reinterpret_cast<f32x4 *>(dst + row) = o[dt];
+        }
+    }
+    __syncthreads();
+
+    constexpr int VEC = QDT == F32 ? 4 : 8;
+    constexpr int PER_HEAD = D / VEC;
+    const float v_scale = P.v_scale;
+    for (int idx = tid; idx < nh * PER_HEAD; idx += WAVES * 64) {
+        const int hh = idx / PER_HEAD;
+        const int d0 = (idx - hh * PER_HEAD) * VEC;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w2 = 0; w2 < WAVES; ++w2) M = fmaxf(M, s_m[w2 * kMaxHeadsPerGroup + hh]);
+        float f[WAVES];
+        float l = 0.0f, lr = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < WAVES; ++w2) {
+            const float mw = s_m[w2 * kMaxHeadsPerGroup + hh];
+            f[w2] = mw == -INFINITY ? 0.0f : exp2_fast(mw - M);
+            l += f[w2] * s_l[w2 * kMaxHeadsPerGroup + hh];
+            lr += f[w2] * s_lr[w2 * kMaxHeadsPerGroup + hh];
+        }
+        const float inv = v_scale / lr;
+        float r[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            float a = 0.0f;
+#pragma unroll
+            for (int w2 = 0; w2 < WAVES; ++w2) a += f[w2] * s_o[(w2 * heads_alloc + hh) * RS + d0 + e];
+            r[e] = a * inv;
+        }
+        const int h = h0 + hh;
+        const int64_t srow = (int64_t)s * P.num_heads + h;
+        uint8_t *dst = reinterpret_cast<uint8_t *>(P.tmp_out) + ((srow * maxP + p) * D + d0) * QB;
+        if constexpr (QDT == F32) {
+            *reinterpret_cast<f32x4 *>(dst) = f32x4{r[0], r[1], r[2], r[3]};
+        } else {
+            u32x4 pk = {pack2<QDT>(r[0], r[1]), pack2<QDT>(r[2], r[3]), pack2<QDT>(r[4], r[5]),
+                        pack2<QDT>(r[6], r[7])};
+            *reinterpret_cast<u32x4 *>(dst) = pk;
+        }
+        if (d0 == 0) {
+            float mabs = M * kLn2;
+            if (P.alibi != nullptr) mabs += P.alibi[h] * (float)last;
+            P.max_logits[srow * maxP + p] = mabs;
+            P.exp_sums[srow * maxP + p] = l;
+        }
+    }
+}
+
+template <int QDT, int KVDT, int D>
+hipError_t launch_one(const Phase1Params &p, int lds, hipStream_t stream) {
+    constexpr int WAVES = kPhase1Waves;
+    constexpr int PF = 2;
+    const int grid = (p.num_work + 7) / 8 * 8;
+    if (lds > 65536)
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, PF>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, PF>), dim3(grid), dim3(WAVES * 64),
+                       lds, stream, p);
+    return hipGetLastError();
+}
+
+template <int QDT, int KVDT>
+hipError_t launch_d(const Phase1Params &p, int D, int lds, hipStream_t stream) {
+    switch (D) {
+    case 64: return launch_one<QDT, KVDT, 64>(p, lds, stream);
+    case 80: return launch_one<QDT, KVDT, 80>(p, lds, stream);
+    case 96: return launch_one<QDT, KVDT, 96>(p, lds, stream);
+    case 112: return launch_one<QDT, KVDT, 112>(p, lds, stream);
+    case 128: return launch_one<QDT, KVDT, 128>(p, lds, stream);
+    case 192: return launch_one<QDT, KVDT, 192>(p, lds, stream);
+    case 256: return launch_one<QDT, KVDT, 256>(p, lds, stream);
+    case 120:
+        if constexpr (KVDT != FP8) return launch_one<QDT, KVDT, 120>(p, lds, stream);
+        else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_phase1(const Phase1Params &p, int qdt, int kvdt, int head_size, int waves,
+                         int lds_bytes, hipStream_t stream) {
+    if (waves != kPhase1Waves) return hipErrorInvalidValue;
+    if (qdt == F32 && kvdt == F32) return launch_d<F32, F32>(p, head_size, lds_bytes, stream);
+    if (qdt == F16 && kvdt == F16) return launch_d<F16, F16>(p, head_size, lds_bytes, stream);
+    if (qdt == BF16 && kvdt == BF16) return launch_d<BF16, BF16>(p, head_size, lds_bytes, stream);
+    if (qdt == F32 && kvdt == FP8) return launch_d<F32, FP8>(p, head_size, lds_bytes, stream);
+    if (qdt == F16 && kvdt == FP8) return launch_d<F16, FP8>(p, head_size, lds_bytes, stream);
+    if (qdt == BF16 && kvdt == FP8) return launch_d<BF16, FP8>(p, head_size, lds_bytes, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pav2

@@ -1,0 +1,181 @@
+/*
+ * pav2.h -- PagedAttention V2 decode on AMD MI355X (gfx950): C ABI.
+ *
+ * The operation (page "paged_attention_v2_pytorch.py", function
+ * paged_attention_v2_pytorch, and its signature comments): for every sequence
+ * s and query head h, single-query attention of query[s, h, :] over the
+ * sequence's first seq_lens[s] cached tokens, read through the block table,
+ * computed in two phases:
+ *
+ *   phase 1, per 512-token partition p of the context (partition bounds as in
+ *   page "paged_attention_v2_triton.py", part_start / part_end):
+ *     z_t        = scale * (q . K_t) + alibi_slopes[h] * t      (t absolute, 0-based)
+ *     m_p        = max_t z_t                      -> max_logits[s, h, p]
+ *     l_p        = sum_t exp(z_t - m_p)           -> exp_sums[s, h, p]
+ *     o_p        = sum_t exp(z_t - m_p) V_t / l_p -> tmp_output[s, h, p, :]
+ *   phase 2, the log-sum-exp combine (page 1, "Cross-partition reduction";
+ *   page 2, _paged_attn_v2_reduce_kernel):
+ *     M = max_p m_p,  w_p = exp(m_p - M) * l_p,  out = sum_p w_p o_p / sum_p w_p.
+ *
+ * K_t and V_t are the key / value rows of kv head h / (num_heads /
+ * num_kv_heads) (grouped-query attention without expanding K/V), gathered from
+ * block block_tables[s, t / block_size], slot t % block_size, multiplied by
+ * k_scale / v_scale.  tmp_output holds each partition's own normalised output
+ * o_p (the reading under which the pages' phase-2 weights give softmax(z) V).
+ *
+ * Layouts (all row-major, contiguous, device memory owned by the caller):
+ *   query        [num_seqs, num_heads, head_size]                  query_dtype
+ *   key_cache    [num_blocks, num_kv_heads, head_size/x, block_size, x]
+ *                x = 16 / sizeof(kv element): one 16-byte vector holds x
+ *                consecutive head-dim elements of one token     kv_cache_dtype
+ *   value_cache  [num_blocks, num_kv_heads, head_size, block_size] kv_cache_dtype
+ *   block_tables [num_seqs, max_blocks_per_seq] int32 physical block ids;
+ *                entries past a sequence's last block are never read
+ *   seq_lens     [num_seqs] int32, 0 <= seq_lens[s] <= max_seq_len
+ *   alibi_slopes [num_heads] float32, or NULL for no ALiBi
+ *   output       [num_seqs, num_heads, head_size]                  query_dtype
+ *   exp_sums     [num_seqs, num_heads, max_num_partitions]         float32
+ *   max_logits   [num_seqs, num_heads, max_num_partitions]         float32
+ *   tmp_output   [num_seqs, num_heads, max_num_partitions, head_size] query_dtype
+ *
+ * Slots p >= ceil(seq_lens[s] / 512) get max_logits = -inf and exp_sums = 0;
+ * their tmp_output rows are left unwritten.  seq_lens[s] == 0 gives a zero
+ * output row.
+ *
+ * Execution: every call is asynchronous on `stream` (a hipStream_t, NULL for
+ * the null stream); the library never synchronises the host, never reads
+ * device data on the host, and allocates no memory.  Device-side data (block
+ * ids < num_blocks, seq_lens <= max_blocks_per_seq * block_size) is not
+ * checked.
+ *
+ * Errors: every entry point returns PAV2_OK (0) or a negative status and
+ * launches nothing on failure; pav2_last_error() gives the calling thread's
+ * last message.  No C++ exception crosses this interface.
+ */
+#ifndef PAV2_H
+#define PAV2_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PAV2_PARTITION_SIZE 512
+#define PAV2_VERSION 10000 /* 1.0.0 */
+
+typedef enum {
+    PAV2_F32 = 0,       /* IEEE binary32 */
+    PAV2_F16 = 1,       /* IEEE binary16 */
+    PAV2_BF16 = 2,      /* bfloat16 */
+    PAV2_FP8_E4M3 = 3   /* OCP fp8 E4M3 ("e4m3fn"), KV cache only */
+} pav2_dtype_t;
+
+enum {
+    PAV2_OK = 0,
+    PAV2_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, inconsistent shape */
+    PAV2_ERR_UNSUPPORTED = -2,      /* valid but not implemented (dtype pair, head size) */
+    PAV2_ERR_LAUNCH = -3            /* the HIP runtime refused a launch */
+};
+
+typedef void *pav2_stream_t; /* hipStream_t */
+
+/*
+ * Both phases, stream-ordered: phase 1 writes exp_sums, max_logits and
+ * tmp_output; phase 2 reads them and writes output.
+ *
+ * Argument order follows the pages' V2 op (output, exp_sums, max_logits,
+ * tmp_output, query, key_cache, value_cache, num_kv_heads, scale,
+ * block_tables, seq_lens, block_size, max_seq_len, alibi_slopes,
+ * kv_cache_dtype, k_scale, v_scale); the shapes the pages read from tensor
+ * metadata follow, then the query dtype and the stream.
+ *
+ * Supported: head_size in {64, 80, 96, 112, 120, 128, 192, 256} (the pages'
+ * supported head sizes) with head_size % x == 0; block_size a power of two in
+ * [4, 512] (512 % block_size == 0); num_heads % num_kv_heads == 0;
+ * (query_dtype, kv_cache_dtype) in {(F32, F32), (F16, F16), (BF16, BF16),
+ * (F32, FP8_E4M3), (F16, FP8_E4M3), (BF16, FP8_E4M3)};
+ * max_num_partitions >= ceil(max_seq_len / 512) and <= 16384;
+ * max_blocks_per_seq >= ceil(max_seq_len / block_size).
+ */
+int pav2_paged_attention_v2(
+    void *output, float *exp_sums, float *max_logits, void *tmp_output,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_kv_heads, float scale,
+    const int32_t *block_tables, const int32_t *seq_lens,
+    int block_size, int max_seq_len,
+    const float *alibi_slopes,
+    pav2_dtype_t kv_cache_dtype, float k_scale, float v_scale,
+    int num_seqs, int num_heads, int head_size, int num_blocks,
+    int max_blocks_per_seq, int max_num_partitions,
+    pav2_dtype_t query_dtype,
+    pav2_stream_t stream);
+
+/*
+ * Phase 1 alone (same arguments as above without `output`): writes
+ * exp_sums, max_logits and tmp_output.
+ */
+int pav2_phase1(
+    float *exp_sums, float *max_logits, void *tmp_output,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_kv_heads, float scale,
+    const int32_t *block_tables, const int32_t *seq_lens,
+    int block_size, int max_seq_len,
+    const float *alibi_slopes,
+    pav2_dtype_t kv_cache_dtype, float k_scale, float v_scale,
+    int num_seqs, int num_heads, int head_size, int num_blocks,
+    int max_blocks_per_seq, int max_num_partitions,
+    pav2_dtype_t query_dtype,
+    pav2_stream_t stream);
+
+/*
+ * Phase 2 alone, the log-sum-exp combine: reads exp_sums, max_logits and
+ * tmp_output for partitions p < min(ceil(seq_lens[s]/512), max_num_partitions)
+ * and writes output (dtype `out_dtype`, which is also tmp_output's dtype).
+ */
+int pav2_phase2(
+    void *output, const float *exp_sums, const float *max_logits,
+    const void *tmp_output, const int32_t *seq_lens,
+    int num_seqs, int num_heads, int head_size, int max_num_partitions,
+    pav2_dtype_t out_dtype, pav2_stream_t stream);
+
+/* Launch plan the library would use for a problem (host only, no GPU call). */
+typedef struct {
+    int phase1_workgroups;    /* phase-1 grid size */
+    int phase1_threads;       /* threads per phase-1 workgroup */
+    int phase1_lds_bytes;     /* dynamic LDS per phase-1 workgroup */
+    int head_groups;          /* ceil(gqa / 16): query-head groups per kv head */
+    int waves_per_partition;  /* wavefronts sharing one 512-token partition */
+    int phase2_workgroups;
+    int phase2_threads;
+    int phase2_lds_bytes;
+} pav2_plan_t;
+
+int pav2_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+              int block_size, int max_num_partitions,
+              pav2_dtype_t query_dtype, pav2_dtype_t kv_cache_dtype,
+              pav2_plan_t *plan);
+
+/*
+ * Widen n KV-cache elements of `kv_dtype` to float32 on the device with the
+ * conversion phase 1 applies when its MFMA operands are `compute_dtype`
+ * (the query dtype; only meaningful for FP8_E4M3 caches, which are widened
+ * to f32, f16 or bf16 in registers).  src, dst are device pointers.  A test
+ * hook for the device-side element decoding.
+ */
+int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype,
+                   pav2_dtype_t compute_dtype, pav2_stream_t stream);
+
+/* ceil(max_seq_len / 512): the partition count a sequence of that length needs. */
+int pav2_max_num_partitions(int max_seq_len);
+
+/* The calling thread's last error message ("" if none). */
+const char *pav2_last_error(void);
+
+int pav2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAV2_H */

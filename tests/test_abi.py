@@ -1,0 +1,141 @@
+"""C-ABI library checks that need no GPU: it loads, exports every function
+include/pav2.h declares, rejects invalid arguments with the documented status
+before touching the device, and plans launches on the host."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_paged_v2_amd as pav2
+from decode_attention_paged_v2_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pav2.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pav2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = pav2.load()
+    names = declared_functions()
+    assert "pav2_paged_attention_v2" in names and len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared in pav2.h but not exported"
+    assert pav2.version() == 10000
+
+
+def test_max_num_partitions():
+    assert pav2.max_num_partitions(0) == 0
+    assert pav2.max_num_partitions(1) == 1
+    assert pav2.max_num_partitions(512) == 1
+    assert pav2.max_num_partitions(513) == 2
+    # 100K context: the page's "195 x bmm" is a floor slip, ceil gives 196
+    assert pav2.max_num_partitions(100000) == 196
+
+
+def _call(**over):
+    """pav2_phase1/full call with host-only (null) pointers and overridable sizes."""
+    lib = pav2.load()
+    a = dict(output=ctypes.c_void_p(16), exp_sums=ctypes.c_void_p(16), max_logits=ctypes.c_void_p(16),
+             tmp_output=ctypes.c_void_p(16), query=ctypes.c_void_p(16), key_cache=ctypes.c_void_p(16),
+             value_cache=ctypes.c_void_p(16), num_kv_heads=4, scale=0.0625,
+             block_tables=ctypes.c_void_p(16), seq_lens=ctypes.c_void_p(16), block_size=16,
+             max_seq_len=100000, alibi_slopes=None, kv_cache_dtype=B.BF16, k_scale=1.0, v_scale=1.0,
+             num_seqs=4, num_heads=24, head_size=256, num_blocks=25000, max_blocks_per_seq=6250,
+             max_num_partitions=196, query_dtype=B.BF16, stream=None)
+    a.update(over)
+    return lib.pav2_paged_attention_v2(*a.values())
+
+
+# Each case is invalid, so the call must return before any HIP call.
+INVALID = [
+    (dict(num_heads=25), -1, "multiple of num_kv_heads"),
+    (dict(num_kv_heads=0), -1, "must be > 0"),
+    (dict(head_size=100), -2, "head_size 100"),
+    (dict(head_size=120, kv_cache_dtype=B.FP8_E4M3), -2, "multiple of x = 16"),
+    (dict(block_size=24), -1, "block_size 24"),
+    (dict(block_size=1024), -1, "block_size 1024"),
+    (dict(block_size=2), -1, "block_size 2"),
+    (dict(max_num_partitions=195), -1, "ceil(max_seq_len / 512) = 196"),
+    (dict(max_blocks_per_seq=6249), -1, "max_blocks_per_seq"),
+    (dict(query_dtype=B.F16), -2, "query dtype f16 with kv dtype bf16"),
+    (dict(query_dtype=B.FP8_E4M3, kv_cache_dtype=B.FP8_E4M3), -1, "query dtype"),
+    (dict(kv_cache_dtype=9), -1, "unknown kv_cache_dtype"),
+    (dict(output=None), -1, "output is NULL"),
+    (dict(query=None), -1, "NULL"),
+    (dict(block_tables=None), -1, "NULL"),
+    (dict(scale=float("nan")), -1, "finite"),
+    (dict(k_scale=float("inf")), -1, "finite"),
+    (dict(num_blocks=0), -1, "num_blocks"),
+    (dict(max_seq_len=-1), -1, "max_seq_len"),
+    (dict(num_seqs=-1), -1, "num_seqs"),
+    (dict(max_num_partitions=20000, max_seq_len=20000 * 512, max_blocks_per_seq=640000), -2, "exceeds"),
+]
+
+
+@pytest.mark.parametrize("over,status,msg", INVALID)
+def test_invalid_arguments_are_rejected(over, status, msg):
+    assert _call(**over) == status
+    assert msg in pav2.last_error()
+
+
+def test_zero_sequences_is_a_no_op():
+    assert _call(num_seqs=0, output=None, query=None) == 0
+    assert pav2.last_error() == ""
+
+
+def test_phase2_validation():
+    lib = pav2.load()
+    v = ctypes.c_void_p(16)
+    assert lib.pav2_phase2(v, v, v, v, v, 4, 24, 100, 196, B.BF16, None) == -2
+    assert lib.pav2_phase2(v, v, v, v, v, 4, 24, 256, 0, B.BF16, None) == -1
+    assert lib.pav2_phase2(v, v, v, v, v, 4, 24, 256, 196, B.FP8_E4M3, None) == -1
+    assert lib.pav2_phase2(None, v, v, v, v, 4, 24, 256, 196, B.BF16, None) == -1
+    assert lib.pav2_phase2(None, None, None, None, None, 0, 24, 256, 196, B.BF16, None) == 0
+
+
+def test_decode_kv_validation():
+    lib = pav2.load()
+    v = ctypes.c_void_p(16)
+    assert lib.pav2_decode_kv(v, v, -1, B.FP8_E4M3, B.BF16, None) == -1
+    assert lib.pav2_decode_kv(None, v, 5, B.FP8_E4M3, B.BF16, None) == -1
+    assert lib.pav2_decode_kv(v, v, 5, B.FP8_E4M3, B.FP8_E4M3, None) == -1
+    assert lib.pav2_decode_kv(v, v, 0, B.FP8_E4M3, B.BF16, None) == 0
+
+
+@pytest.mark.parametrize("cfg,expect", [
+    # long-context GQA: 4 seqs x 4 kv heads x 196 partitions, 6 query heads per kv head
+    (dict(num_seqs=4, num_heads=24, num_kv_heads=4, head_size=256, block_size=16,
+          max_num_partitions=196, query_dtype=B.BF16, kv_cache_dtype=B.BF16),
+     dict(phase1_workgroups=3136, head_groups=1, phase2_workgroups=96)),
+    # fp8 KV: 64 x 8 x 32
+    (dict(num_seqs=64, num_heads=64, num_kv_heads=8, head_size=128, block_size=32,
+          max_num_partitions=32, query_dtype=B.BF16, kv_cache_dtype=B.FP8_E4M3),
+     dict(phase1_workgroups=16384, head_groups=1, phase2_workgroups=4096)),
+    # 32 query heads per kv head need two 16-head groups; grid rounded up to 8
+    (dict(num_seqs=3, num_heads=32, num_kv_heads=1, head_size=128, block_size=16,
+          max_num_partitions=3, query_dtype=B.F16, kv_cache_dtype=B.F16),
+     dict(phase1_workgroups=24, head_groups=2, phase2_workgroups=96)),
+])
+def test_plan(cfg, expect):
+    p = pav2.plan(**cfg)
+    for k, v in expect.items():
+        assert p[k] == v, (k, p)
+    assert p["phase1_threads"] == 256 and p["phase2_threads"] == 256
+    assert 0 < p["phase1_lds_bytes"] <= 160 * 1024
+    assert 0 < p["phase2_lds_bytes"] <= 160 * 1024
+
+
+def test_python_binding_has_no_cpu_path():
+    import torch
+    q = torch.zeros(1, 4, 64)
+    with pytest.raises(ValueError, match="device tensor"):
+        pav2.paged_attention_v2(q, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1), torch.zeros(1, 4, 1, 64),
+                                q, torch.zeros(2, 4, 16, 16, 4), torch.zeros(2, 4, 64, 16), 4, 0.125,
+                                torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32),
+                                16, 1)
