@@ -35,18 +35,20 @@ class Plan(ctypes.Structure):
 
 
 def lib_path() -> str:
-    return _build.LIB
+    """The library this process loads: $PAV2_LIBRARY if set, else the in-tree build."""
+    return os.environ.get("PAV2_LIBRARY") or _build.LIB
 
 
 def load():
-    """Load libpav2.so (building it first only if no library exists)."""
+    """Load libpav2.so (building the in-tree one first only if none exists)."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_build.LIB):
+        path = lib_path()
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         attn = [P, P, P, P, P, P, P, I, F, P, P, I, I, P, I, F, F, I, I, I, I, I, I, I, P]
         L.pav2_paged_attention_v2.argtypes = attn

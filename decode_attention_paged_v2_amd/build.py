@@ -29,8 +29,8 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, extra=()) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
+def _compile(src: str, extra=(), build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(os.path.basename(src))[0] + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -38,19 +38,20 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile and link; ``extra`` adds hipcc flags (e.g. -DPAV2_PHASE1_WAVES=8)."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 def is_stale() -> bool:

@@ -75,8 +75,25 @@ hipError_t launch_phase2(const Phase2Params &p, int odt, int head_size, int thre
 hipError_t launch_decode_kv(const void *src, float *dst, int64_t n, int dtype, int via,
                             hipStream_t stream);
 
-// Phase-1 workgroup shape.
-constexpr int kPhase1Waves = 4;
+// Phase-1 workgroup shape: wavefronts per workgroup, tiles of loads in flight
+// per wavefront, minimum wavefronts per SIMD the register budget must allow,
+// and whether K/V loads carry the non-temporal (streaming) hint.
+#ifndef PAV2_PHASE1_WAVES
+#define PAV2_PHASE1_WAVES 4
+#endif
+#ifndef PAV2_PHASE1_PREFETCH
+#define PAV2_PHASE1_PREFETCH 2
+#endif
+#ifndef PAV2_PHASE1_OCCUPANCY
+#define PAV2_PHASE1_OCCUPANCY 1
+#endif
+#ifndef PAV2_PHASE1_NONTEMPORAL
+#define PAV2_PHASE1_NONTEMPORAL 1
+#endif
+constexpr int kPhase1Waves = PAV2_PHASE1_WAVES;
+constexpr int kPhase1Prefetch = PAV2_PHASE1_PREFETCH;
+constexpr int kPhase1Occupancy = PAV2_PHASE1_OCCUPANCY;
+constexpr bool kPhase1NonTemporal = PAV2_PHASE1_NONTEMPORAL != 0;
 constexpr int kPhase2Threads = 256;
 
 inline int phase1_lds_bytes(int gqa, int head_size, int waves, int bs_log2) {

@@ -143,8 +143,16 @@ struct Words {
     uint32_t w[N];
 };
 
+template <typename T>
+__device__ __forceinline__ T load_stream(const uint8_t *p) {
+    if constexpr (kPhase1NonTemporal)
+        return __builtin_nontemporal_load(reinterpret_cast<const T *>(p));
+    else
+        return *reinterpret_cast<const T *>(p);
+}
+
 template <int QDT, int KVDT, int D, int WAVES, int PF>
-__global__ void __launch_bounds__(WAVES * 64)
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(kPhase1Occupancy)))
 phase1_kernel(const Phase1Params P) {
     using S = Shape<QDT, KVDT, D>;
     constexpr int TPW = kTilesPerPartition / WAVES;   // tiles per wavefront
@@ -254,7 +262,7 @@ phase1_kernel(const Phase1Params P) {
         for (int u = 0; u < NKL; ++u) {
             u32x4 v = {0, 0, 0, 0};
             if (4 * u + grp < S::kChunks)
-                v = *reinterpret_cast<const u32x4 *>(base + ((int64_t)(4 * u) << (bs_log2 + 4)));
+                v = load_stream<u32x4>(base + ((int64_t)(4 * u) << (bs_log2 + 4)));
             dst[u] = v;
         }
     };
@@ -268,15 +276,15 @@ phase1_kernel(const Phase1Params P) {
             const uint8_t *ptr = base + ((int64_t)(16 * dt) << bs_log2) * KVB;
             const bool ok = (D % 16 == 0) || (16 * dt + col < D);
             if constexpr (S::kVWords == 1) {
-                dst[dt].w[0] = ok ? *reinterpret_cast<const uint32_t *>(ptr) : 0u;
+                dst[dt].w[0] = ok ? load_stream<uint32_t>(ptr) : 0u;
             } else if constexpr (S::kVWords == 2) {
                 u32x2 v = {0, 0};
-                if (ok) v = *reinterpret_cast<const u32x2 *>(ptr);
+                if (ok) v = load_stream<u32x2>(ptr);
                 dst[dt].w[0] = v[0];
                 dst[dt].w[1] = v[1];
             } else {
                 u32x4 v = {0, 0, 0, 0};
-                if (ok) v = *reinterpret_cast<const u32x4 *>(ptr);
+                if (ok) v = load_stream<u32x4>(ptr);
                 dst[dt].w[0] = v[0];
                 dst[dt].w[1] = v[1];
                 dst[dt].w[2] = v[2];
@@ -507,7 +515,7 @@ phase1_kernel(const Phase1Params P) {
 template <int QDT, int KVDT, int D>
 hipError_t launch_one(const Phase1Params &p, int lds, hipStream_t stream) {
     constexpr int WAVES = kPhase1Waves;
-    constexpr int PF = 2;
+    constexpr int PF = kPhase1Prefetch;
     const int grid = (p.num_work + 7) / 8 * 8;
     if (lds > 65536)
         hipFuncSetAttribute(reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, PF>),
