@@ -112,6 +112,24 @@ def cpu_baseline(wl, out_gpu, target_core_seconds=15.0, max_threads=16):
     }
 
 
+def copy_reference(dev, steps, warmup, nbytes=1 << 30):
+    """A plain device-to-device copy of nbytes: reads nbytes, writes nbytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "ms": round(ms, 5),
+            "read_plus_write_GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +139,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="extra per-step timings with a 1 GiB cache flush before each step")
+    ap.add_argument("--mode", default="decode", choices=["decode", "copy"],
+                    help="copy: time a plain 1 GiB device copy (the reference kernel for "
+                         "scaling HBM byte counters and for achievable bandwidth)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -133,6 +154,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mode == "copy":
+        print(json.dumps(copy_reference(dev, args.steps, args.warmup)), flush=True)
+        return
     pav2.load()
     spec = W.SPECS[args.config]
     t0 = time.time()

@@ -85,9 +85,9 @@ int check_shape(const Shape &s) {
     if (s.kvdt != s.qdt && s.kvdt != PAV2_FP8_E4M3)
         return fail(PAV2_ERR_UNSUPPORTED, "query dtype %s with kv dtype %s is not supported",
                     dt_name(s.qdt), dt_name(s.kvdt));
-    if (ilog2_exact(s.block_size) < 2 || PAV2_PARTITION_SIZE % s.block_size)
+    if (ilog2_exact(s.block_size) < 3 || PAV2_PARTITION_SIZE % s.block_size)
         return fail(PAV2_ERR_INVALID_ARGUMENT,
-                    "block_size %d must be a power of two in [4, 512] dividing the 512-token partition",
+                    "block_size %d must be a power of two in [8, 512] dividing the 512-token partition",
                     s.block_size);
     if (s.num_blocks <= 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
     if (s.max_seq_len < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 0");

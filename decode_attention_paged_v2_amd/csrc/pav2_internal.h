@@ -8,8 +8,6 @@
 namespace pav2 {
 
 constexpr int kPartition = 512;                 // tokens per partition
-constexpr int kTile = 16;                       // tokens per MFMA tile
-constexpr int kTilesPerPartition = kPartition / kTile;
 constexpr int kMaxHeadsPerGroup = 16;           // query heads per MFMA N-tile
 constexpr int kMaxPartitions = 16384;
 
@@ -75,14 +73,11 @@ hipError_t launch_phase2(const Phase2Params &p, int odt, int head_size, int thre
 hipError_t launch_decode_kv(const void *src, float *dst, int64_t n, int dtype, int via,
                             hipStream_t stream);
 
-// Phase-1 workgroup shape: wavefronts per workgroup, tiles of loads in flight
-// per wavefront, minimum wavefronts per SIMD the register budget must allow,
-// and whether K/V loads carry the non-temporal (streaming) hint.
+// Phase-1 workgroup shape: wavefronts per workgroup, minimum wavefronts per
+// SIMD the register budget must allow, and whether K/V loads carry the
+// non-temporal (streaming) hint.
 #ifndef PAV2_PHASE1_WAVES
 #define PAV2_PHASE1_WAVES 4
-#endif
-#ifndef PAV2_PHASE1_PREFETCH
-#define PAV2_PHASE1_PREFETCH 2
 #endif
 #ifndef PAV2_PHASE1_OCCUPANCY
 #define PAV2_PHASE1_OCCUPANCY 1
@@ -91,7 +86,6 @@ hipError_t launch_decode_kv(const void *src, float *dst, int64_t n, int dtype, i
 #define PAV2_PHASE1_NONTEMPORAL 1
 #endif
 constexpr int kPhase1Waves = PAV2_PHASE1_WAVES;
-constexpr int kPhase1Prefetch = PAV2_PHASE1_PREFETCH;
 constexpr int kPhase1Occupancy = PAV2_PHASE1_OCCUPANCY;
 constexpr bool kPhase1NonTemporal = PAV2_PHASE1_NONTEMPORAL != 0;
 constexpr int kPhase2Threads = 256;

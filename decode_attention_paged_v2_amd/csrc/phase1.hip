@@ -14,29 +14,30 @@
 // * Scores are S^T = K Q^T on 16x16 MFMA tiles: 16 tokens (M) x 16 query
 //   heads (N), contracting over the head dimension.  In the key-cache layout
 //   [.., d/x, block_size, x] one 16-byte vector is x consecutive head-dim
-//   elements of one token, which is exactly one lane's A-operand slice for a
-//   16x16x32 (16-bit) step, so K goes from HBM straight into MFMA registers:
-//   per step the wavefront reads 64 such vectors (1 KB, contiguous when the
-//   block size is 16).
-// * The S^T accumulator leaves each lane holding 4 consecutive tokens of one
-//   head, which is exactly the B-operand slice of a 16x16x16 step of
-//   O^T = V^T P^T; V^T's A-operand slice (4 consecutive tokens of one head-dim
-//   row) is one 8-byte load from the value-cache layout [.., d, block_size].
-//   No LDS traffic or lane shuffles sit between the two products.
+//   elements of one token, which is exactly one lane's A-operand slice of a
+//   16x16x32 (16-bit) step, so K goes from HBM straight into MFMA registers.
+// * Tokens are taken 32 at a time as two natural 16-token S^T tiles (K loads
+//   stay whole 16-byte vectors of consecutive tokens).  Two cross-lane swaps
+//   (v_permlane32_swap, v_permlane16_swap) regroup the scores so each lane
+//   holds 8 consecutive tokens of one head: its B-operand slice of a K = 32
+//   step of O^T = V^T P^T, whose A-operand slice (the same 8 tokens of one
+//   head-dim row) is one contiguous load from the value layout
+//   [.., d, block_size]; a lane group's slices cover whole rows.  No LDS
+//   traffic sits between the two products.
 // * The query heads that share a kv head (GQA) are the N dimension, so each
 //   K/V byte is read once per kv head, not once per query head.
-// * Two passes per wavefront: all scores of its tiles first (registers), then
+// * Two passes per wavefront: all scores of its units first (registers), then
 //   one max, then exp and P V with no running rescale.  The wavefronts of a
-//   workgroup split the partition's 16-token tiles round-robin and merge their
+//   workgroup split the partition's units round-robin and merge their
 //   (max, sum, output) once through LDS at the end.
-// * Loads run PF tiles ahead of the MFMAs (K, then V, as one stream), so V
-//   loads are in flight while the score max is reduced.
+// * K and V loads form one stream of load groups issued a few groups ahead of
+//   the MFMAs, so V loads are in flight while the score max is reduced; they
+//   carry the non-temporal hint (each byte is read once).
+// * P is split into two 16-bit parts (hi + lo) that enter two MFMAs against
+//   the same V slice, so the weights keep ~16 significant bits.
 // * fp8 e4m3 caches are widened in registers by the hardware converters to
 //   the query's 16-bit type (exact) or to f32; k_scale folds into the score
 //   scale and v_scale into the final division.
-// * P is split into two 16-bit parts (hi + lo) that enter one 16x16x32 MFMA
-//   against the V slice duplicated, so the weights keep ~16 significant bits
-//   at the MFMA count of a single 16x16x16 product.
 // * exp2 with log2(e) folded into the score scale; ALiBi is added relative to
 //   the partition's last token (bias slope * (t - last), |t - last| < 512, so
 //   scores stay small where they matter), and the stored max_logits are
@@ -134,8 +135,6 @@ struct Shape {
     static constexpr int kKLoads = (kChunks + 3) / 4;   // K vectors per lane per tile
     static constexpr int kDTiles = (D + 15) / 16;       // 16-row head-dim tiles for P V
     static constexpr int kD16 = kDTiles * 16;
-    // V^T slice of one lane per head-dim tile: 4 tokens of one row.
-    static constexpr int kVWords = (4 * kKvBytes + 3) / 4;   // 32-bit words per slice
 };
 
 template <int N>
@@ -151,11 +150,10 @@ __device__ __forceinline__ T load_stream(const uint8_t *p) {
         return *reinterpret_cast<const T *>(p);
 }
 
-template <int QDT, int KVDT, int D, int WAVES, int PF>
+template <int QDT, int KVDT, int D, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(kPhase1Occupancy)))
 phase1_kernel(const Phase1Params P) {
     using S = Shape<QDT, KVDT, D>;
-    constexpr int TPW = kTilesPerPartition / WAVES;   // tiles per wavefront
     constexpr int NKL = S::kKLoads;
     constexpr int NDT = S::kDTiles;
     constexpr int X = S::kX;
@@ -197,7 +195,6 @@ phase1_kernel(const Phase1Params P) {
     }
     const int n_tok = min(kPartition, L - start);
     const int last = start + n_tok - 1;   // ALiBi reference position: the partition's last token
-    const int ntiles = (n_tok + kTile - 1) / kTile;
 
     // LDS: per-wave partial outputs, per-wave max/sum, block-table slice.
     const int heads_alloc = min(P.gqa, kMaxHeadsPerGroup);
@@ -247,48 +244,66 @@ phase1_kernel(const Phase1Params P) {
     const uint8_t *vc = P.value_cache + (int64_t)g * P.head_stride;
     const int64_t blk_stride = P.blk_stride;
 
-    // Tile k of this wavefront: partition tile wv + WAVES * k, clamped to
-    // tile 0 when past the end (its tokens are then all masked).
-    auto tile_of = [&](int k) { return wv + WAVES * k; };
-    auto clamp_tile = [&](int t) { return t < ntiles ? t : 0; };
+    // The partition is processed in 32-token units, assigned to the wavefronts
+    // round-robin; a unit past the end is clamped to unit 0 (its tokens are
+    // then all masked).
+    constexpr int UNIT = 32;
+    constexpr int UPW = (kPartition / UNIT) / WAVES;       // units per wavefront
+    const int nunits = (n_tok + UNIT - 1) / UNIT;
+    auto unit_of = [&](int u) { return wv + WAVES * u; };
+    auto clamp_unit = [&](int t) { return t < nunits ? t : 0; };
+
+    // Load groups: K of a unit in KG groups (halves when large), V of a unit in
+    // VSPLIT groups of head-dim tiles; the loads run PF groups ahead of use.
+    constexpr int VW = 8 * KVB / 4;                        // words per V slice (8 tokens)
+    constexpr int KG = (2 * NKL * 4 > 32) ? 2 : 1;
+    constexpr int KH = 2 / KG;                             // K halves per group
+    constexpr int VSPLIT = (NDT * VW > 32) ? 2 : 1;
+    constexpr int DPG = (NDT + VSPLIT - 1) / VSPLIT;       // head-dim tiles per V group
+    constexpr int GK = UPW * KG;
+    constexpr int NG = GK + UPW * VSPLIT;
+    constexpr int PF = (KH * NKL * 4 <= 16 && DPG * VW <= 16) ? 3 : 2;
 
     // ---- load helpers ----------------------------------------------------
-    auto load_k = [&](u32x4 (&dst)[NKL], int k) {
-        const int t = clamp_tile(tile_of(k));
-        const int o = t * kTile + col;                       // token offset in partition
+    auto load_k = [&](u32x4 (&dst)[NKL], int u, int half) {
+        const int t = clamp_unit(unit_of(u));
+        const int o = t * UNIT + 16 * half + col;            // token offset in partition
         const int64_t b = s_bt[o >> bs_log2];
         const uint8_t *base = kc + b * blk_stride + (o & bs_mask) * 16 + (grp << (bs_log2 + 4));
 #pragma unroll
-        for (int u = 0; u < NKL; ++u) {
+        for (int w = 0; w < NKL; ++w) {
             u32x4 v = {0, 0, 0, 0};
-            if (4 * u + grp < S::kChunks)
-                v = load_stream<u32x4>(base + ((int64_t)(4 * u) << (bs_log2 + 4)));
-            dst[u] = v;
+            if (4 * w + grp < S::kChunks)
+                v = load_stream<u32x4>(base + ((int64_t)(4 * w) << (bs_log2 + 4)));
+            dst[w] = v;
         }
     };
-    auto load_v = [&](Words<S::kVWords> (&dst)[NDT], int k) {
-        const int t = clamp_tile(tile_of(k));
-        const int o = t * kTile + 4 * grp;                   // first of the lane's 4 tokens
+    auto load_v = [&](Words<VW> (&dst)[DPG], int u, int part) {
+        const int t = clamp_unit(unit_of(u));
+        const int o = t * UNIT + 8 * grp;                    // first of the lane's 8 tokens
         const int64_t b = s_bt[o >> bs_log2];
         const uint8_t *base = vc + b * blk_stride + (o & bs_mask) * KVB + (col << bs_log2) * KVB;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
+        for (int i = 0; i < DPG; ++i) {
+            const int dt = part * DPG + i;
+            if (dt >= NDT) break;
             const uint8_t *ptr = base + ((int64_t)(16 * dt) << bs_log2) * KVB;
             const bool ok = (D % 16 == 0) || (16 * dt + col < D);
-            if constexpr (S::kVWords == 1) {
-                dst[dt].w[0] = ok ? load_stream<uint32_t>(ptr) : 0u;
-            } else if constexpr (S::kVWords == 2) {
+            if constexpr (VW == 2) {
                 u32x2 v = {0, 0};
                 if (ok) v = load_stream<u32x2>(ptr);
-                dst[dt].w[0] = v[0];
-                dst[dt].w[1] = v[1];
+                dst[i].w[0] = v[0];
+                dst[i].w[1] = v[1];
             } else {
-                u32x4 v = {0, 0, 0, 0};
-                if (ok) v = load_stream<u32x4>(ptr);
-                dst[dt].w[0] = v[0];
-                dst[dt].w[1] = v[1];
-                dst[dt].w[2] = v[2];
-                dst[dt].w[3] = v[3];
+#pragma unroll
+                for (int h = 0; h < VW / 4; ++h) {
+                    u32x4 v = {0, 0, 0, 0};
+                    if (ok) v = load_stream<u32x4>(ptr + 16 * h);
+                    dst[i].w[4 * h + 0] = v[0];
+                    dst[i].w[4 * h + 1] = v[1];
+                    dst[i].w[4 * h + 2] = v[2];
+                    dst[i].w[4 * h + 3] = v[3];
+                }
             }
         }
     };
@@ -312,8 +327,7 @@ phase1_kernel(const Phase1Params P) {
                 acc = mfma_k32<QDT>(k1, q1, acc);
             } else if constexpr (KVDT == F32) {   // f32: four 16x16x4 steps per vector
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc = mfma_k4(as_f32(kr[u][e]), as_f32(qw[u].w[e]), acc);
+                for (int e = 0; e < 4; ++e) acc = mfma_k4(as_f32(kr[u][e]), as_f32(qw[u].w[e]), acc);
             } else {                              // fp8 K with f32 query
 #pragma unroll
                 for (int wd = 0; wd < 4; ++wd) {
@@ -329,121 +343,163 @@ phase1_kernel(const Phase1Params P) {
         return acc;
     };
 
-    // ---- O^T += V^T P^T for one tile -------------------------------------------
     f32x4 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto pv_tile = [&](Words<S::kVWords> (&vr)[NDT], const float (&pr)[4], u32x4 pb, int k) {
-        const int tok0 = start + tile_of(k) * kTile + 4 * grp;   // unclamped
-        const bool partial = start + tile_of(k) * kTile + kTile > L;   // wave-uniform
-        if constexpr (!S::kF32) {
-            uint32_t m0 = 0xffffffffu, m1 = 0xffffffffu;
-            if (partial) {
-                m0 = (tok0 + 0 < L ? 0x0000ffffu : 0u) | (tok0 + 1 < L ? 0xffff0000u : 0u);
-                m1 = (tok0 + 2 < L ? 0x0000ffffu : 0u) | (tok0 + 3 < L ? 0xffff0000u : 0u);
-            }
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                uint32_t a0, a1;
-                if constexpr (KVDT == FP8) {
-                    a0 = fp8x2_to_16<QDT, false>(vr[dt].w[0]);
-                    a1 = fp8x2_to_16<QDT, true>(vr[dt].w[0]);
-                } else {
-                    a0 = vr[dt].w[0];
-                    a1 = vr[dt].w[1];
-                }
-                a0 &= m0;
-                a1 &= m1;
-                // K = 32: the lane's 4 tokens twice, against P's high and low parts
-                const u32x4 a = {a0, a1, a0, a1};
-                o[dt] = mfma_k32<QDT>(a, pb, o[dt]);
-            }
-        } else {
-            bool ok[4] = {true, true, true, true};
-            if (partial) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ok[e] = tok0 + e < L;
-            }
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                float a[4];
-                if constexpr (KVDT == FP8) {
-                    f32x2 lo = fp8x2_to_f32<false>(vr[dt].w[0]);
-                    f32x2 hi = fp8x2_to_f32<true>(vr[dt].w[0]);
-                    a[0] = lo[0]; a[1] = lo[1]; a[2] = hi[0]; a[3] = hi[1];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) a[e] = as_f32(vr[dt].w[e]);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[dt] = mfma_k4(ok[e] ? a[e] : 0.0f, pr[e], o[dt]);
-            }
-        }
-    };
-
-    // ---- one stream of 2*TPW loads (K tiles, then V tiles), PF ahead --------
-    u32x4 kbuf[PF][NKL];
-    Words<S::kVWords> vbuf[PF][NDT];
-    float sc[TPW][4];
+    u32x4 kbuf[PF][KH][NKL];
+    Words<VW> vbuf[PF][DPG];
+    float sc[UPW][8];                 // scores of the lane's 8 tokens per unit (log2 units)
+    const bool has_alibi = P.alibi != nullptr;
 
     auto issue = [&](int j) {
-        if (j < TPW) load_k(kbuf[j % PF], j);
-        else if (j < 2 * TPW) load_v(vbuf[(j - TPW) % PF], j - TPW);
+        if (j < GK) {
+#pragma unroll
+            for (int hh = 0; hh < KH; ++hh) load_k(kbuf[j % PF][hh], j / KG, (j % KG) * KH + hh);
+        } else if (j < NG) {
+            load_v(vbuf[j % PF], (j - GK) / VSPLIT, (j - GK) % VSPLIT);
+        }
     };
 
 #pragma unroll
     for (int j = 0; j < PF; ++j) issue(j);
 
-    // Pass 1: scores.
+    // Pass 1: scores of every unit.  Tile `half` of a unit holds tokens
+    // 16 * half + 4 * grp + i in the lane's accumulator element i.
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-        f32x4 acc = qk_tile(kbuf[k % PF]);
-        issue(k + PF);
-        const int tok0 = start + tile_of(k) * kTile + 4 * grp;
+    for (int j = 0; j < GK; ++j) {
+        const int u = j / KG;
+        f32x4 acc[KH];
+#pragma unroll
+        for (int hh = 0; hh < KH; ++hh) acc[hh] = qk_tile(kbuf[j % PF][hh]);
+        issue(j + PF);
+#pragma unroll
+        for (int hh = 0; hh < KH; ++hh) {
+            const int half = (j % KG) * KH + hh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[u][4 * half + i] = acc[hh][i] * scale_log2;
+        }
+    }
+    // Regroup each unit's scores so that lane group g holds tokens 8g .. 8g+7:
+    // swapping the upper 32 lanes of the first tile with the lower 32 of the
+    // second, then odd 16-lane rows of the first with even rows of the second,
+    // leaves tokens 8g + i in the first register and 8g + 4 + i in the second.
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int tok = tok0 + i;
-            float v = acc[i] * scale_log2 + slope2 * (float)(tok - last);
-            sc[k][i] = tok < L ? v : -INFINITY;
+            const auto r = __builtin_amdgcn_permlane32_swap(as_u32(sc[u][i]), as_u32(sc[u][4 + i]), false, false);
+            const auto q = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+            sc[u][i] = as_f32(q[0]);
+            sc[u][4 + i] = as_f32(q[1]);
+        }
+        const int t0 = start + unit_of(u) * UNIT + 8 * grp;   // unclamped
+        const bool partial = start + unit_of(u) * UNIT + UNIT > L;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = sc[u][e];
+            if (has_alibi) v += slope2 * (float)(t0 + e - last);
+            if (partial) v = (t0 + e < L) ? v : -INFINITY;
+            sc[u][e] = v;
         }
     }
 
     float m = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < TPW; ++k)
+    for (int u = 0; u < UPW; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, sc[k][i]);
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, sc[u][e]);
     m = wave_max(m);
     const float mu = (m == -INFINITY) ? 0.0f : m;
 
     // Pass 2: exp and P V.  lsum is the exact sum of the weights (stored as
-    // exp_sums); lsum_r sums the weights as rounded into the MFMA operand, so
-    // that the partition output is a true weighted mean of V rows.
+    // exp_sums); lsum_r sums the weights as they enter the MFMAs, so that the
+    // partition output is a true weighted mean of V rows.  16-bit operands
+    // carry P as hi + lo, two 16-bit parts (~16 significant bits).
     float lsum = 0.0f, lsum_r = 0.0f;
+    float pr[8];
+    u32x4 ph = {0u, 0u, 0u, 0u}, pl = {0u, 0u, 0u, 0u};
+    uint32_t vmask[4] = {~0u, ~0u, ~0u, ~0u};
+    bool vpartial = false;
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-        float pr[4];
+    for (int j = GK; j < NG; ++j) {
+        const int u = (j - GK) / VSPLIT;
+        const int part = (j - GK) % VSPLIT;
+        if (part == 0) {
+            const int t0 = start + unit_of(u) * UNIT + 8 * grp;
+            vpartial = start + unit_of(u) * UNIT + UNIT > L;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr[i] = exp2_fast(sc[k][i] - mu);
-            lsum += pr[i];
+            for (int e = 0; e < 8; ++e) {
+                pr[e] = exp2_fast(sc[u][e] - mu);
+                lsum += pr[e];
+            }
+            if constexpr (!S::kF32) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t h = pack2<QDT>(pr[2 * k], pr[2 * k + 1]);
+                    const float r0 = pr[2 * k] - unpack_lo<QDT>(h);
+                    const float r1 = pr[2 * k + 1] - unpack_hi<QDT>(h);
+                    const uint32_t l = pack2<QDT>(r0, r1);
+                    ph[k] = h;
+                    pl[k] = l;
+                    lsum_r += (unpack_lo<QDT>(h) + unpack_lo<QDT>(l)) + (unpack_hi<QDT>(h) + unpack_hi<QDT>(l));
+                }
+            }
+            if (vpartial) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    vmask[k] = (t0 + 2 * k < L ? 0x0000ffffu : 0u) | (t0 + 2 * k + 1 < L ? 0xffff0000u : 0u);
+            }
         }
-        u32x4 pb = {0u, 0u, 0u, 0u};
-        if constexpr (!S::kF32) {
-            // P = hi + lo, both 16-bit: the pair carries ~16 significant bits.
-            const uint32_t h01 = pack2<QDT>(pr[0], pr[1]);
-            const uint32_t h23 = pack2<QDT>(pr[2], pr[3]);
-            const float r0 = pr[0] - unpack_lo<QDT>(h01), r1 = pr[1] - unpack_hi<QDT>(h01);
-            const float r2 = pr[2] - unpack_lo<QDT>(h23), r3 = pr[3] - unpack_hi<QDT>(h23);
-            const uint32_t l01 = pack2<QDT>(r0, r1);
-            const uint32_t l23 = pack2<QDT>(r2, r3);
-            pb = u32x4{h01, h23, l01, l23};
-            lsum_r += (unpack_lo<QDT>(h01) + unpack_lo<QDT>(l01)) + (unpack_hi<QDT>(h01) + unpack_hi<QDT>(l01)) +
-                      (unpack_lo<QDT>(h23) + unpack_lo<QDT>(l23)) + (unpack_hi<QDT>(h23) + unpack_hi<QDT>(l23));
+        Words<VW> (&vr)[DPG] = vbuf[j % PF];
+#pragma unroll
+        for (int i = 0; i < DPG; ++i) {
+            const int dt = part * DPG + i;
+            if (dt >= NDT) break;
+            if constexpr (!S::kF32) {
+                u32x4 a;
+                if constexpr (KVDT == FP8) {
+                    a[0] = fp8x2_to_16<QDT, false>(vr[i].w[0]);
+                    a[1] = fp8x2_to_16<QDT, true>(vr[i].w[0]);
+                    a[2] = fp8x2_to_16<QDT, false>(vr[i].w[1]);
+                    a[3] = fp8x2_to_16<QDT, true>(vr[i].w[1]);
+                } else {
+                    a = u32x4{vr[i].w[0], vr[i].w[1], vr[i].w[2], vr[i].w[3]};
+                }
+                if (vpartial) {
+                    a[0] &= vmask[0];
+                    a[1] &= vmask[1];
+                    a[2] &= vmask[2];
+                    a[3] &= vmask[3];
+                }
+                o[dt] = mfma_k32<QDT>(a, ph, o[dt]);
+                o[dt] = mfma_k32<QDT>(a, pl, o[dt]);
+            } else {
+                float a[8];
+                if constexpr (KVDT == FP8) {
+#pragma unroll
+                    for (int wd = 0; wd < 2; ++wd) {
+                        f32x2 lo = fp8x2_to_f32<false>(vr[i].w[wd]);
+                        f32x2 hi = fp8x2_to_f32<true>(vr[i].w[wd]);
+                        a[4 * wd + 0] = lo[0];
+                        a[4 * wd + 1] = lo[1];
+                        a[4 * wd + 2] = hi[0];
+                        a[4 * wd + 3] = hi[1];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a[e] = as_f32(vr[i].w[e]);
+                }
+                if (vpartial) {
+                    const int t0 = start + unit_of(u) * UNIT + 8 * grp;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a[e] = (t0 + e < L) ? a[e] : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[dt] = mfma_k4(a[e], pr[e], o[dt]);
+            }
         }
-        pv_tile(vbuf[k % PF], pr, pb, k);
-        issue(TPW + k + PF);
+        issue(j + PF);
     }
     lsum = wave_sum_groups(lsum);
     if constexpr (S::kF32) lsum_r = lsum;
@@ -515,12 +571,11 @@ phase1_kernel(const Phase1Params P) {
 template <int QDT, int KVDT, int D>
 hipError_t launch_one(const Phase1Params &p, int lds, hipStream_t stream) {
     constexpr int WAVES = kPhase1Waves;
-    constexpr int PF = kPhase1Prefetch;
     const int grid = (p.num_work + 7) / 8 * 8;
     if (lds > 65536)
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, PF>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, PF>), dim3(grid), dim3(WAVES * 64),
+    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES>), dim3(grid), dim3(WAVES * 64),
                        lds, stream, p);
     return hipGetLastError();
 }

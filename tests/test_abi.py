@@ -61,6 +61,7 @@ INVALID = [
     (dict(block_size=24), -1, "block_size 24"),
     (dict(block_size=1024), -1, "block_size 1024"),
     (dict(block_size=2), -1, "block_size 2"),
+    (dict(block_size=4), -1, "block_size 4"),
     (dict(max_num_partitions=195), -1, "ceil(max_seq_len / 512) = 196"),
     (dict(max_blocks_per_seq=6249), -1, "max_blocks_per_seq"),
     (dict(query_dtype=B.F16), -2, "query dtype f16 with kv dtype bf16"),
