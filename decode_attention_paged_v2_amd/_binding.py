@@ -28,7 +28,8 @@ class Pav2Error(RuntimeError):
 class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "phase1_workgroups", "phase1_threads", "phase1_lds_bytes", "head_groups",
-        "waves_per_partition", "phase2_workgroups", "phase2_threads", "phase2_lds_bytes")]
+        "waves_per_partition", "phase2_workgroups", "phase2_threads", "phase2_lds_bytes",
+        "phase1_compact")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -116,9 +116,12 @@ void make_plan(const Shape &s, pav2_plan_t *pl) {
     const int64_t work = (int64_t)s.num_seqs * s.num_kv_heads * hg * s.max_num_partitions;
     pl->head_groups = hg;
     pl->waves_per_partition = pav2::kPhase1Waves;
-    pl->phase1_workgroups = (int)((work + 7) / 8 * 8);
+    const bool compact = pav2::phase1_compact(s.num_seqs);
+    pl->phase1_workgroups = (int)((work + 7) / 8 * 8);   // dense grid; compact runs min(this, resident)
     pl->phase1_threads = pav2::kPhase1Waves * 64;
-    pl->phase1_lds_bytes = pav2::phase1_lds_bytes(gqa, s.head_size, pav2::kPhase1Waves, bs_log2);
+    pl->phase1_lds_bytes =
+        pav2::phase1_lds_bytes(gqa, s.head_size, pav2::kPhase1Waves, bs_log2, s.num_seqs, compact);
+    pl->phase1_compact = compact ? 1 : 0;
     pl->phase2_workgroups = s.num_seqs * s.num_heads;
     pl->phase2_threads = pav2::kPhase2Threads;
     pl->phase2_lds_bytes = pav2::phase2_lds_bytes(s.max_num_partitions, s.head_size, s.qdt);
@@ -156,6 +159,7 @@ int run_phase1(float *exp_sums, float *max_logits, void *tmp_output, const void 
     p.max_blocks_per_seq = sh.max_blocks_per_seq;
     p.max_num_partitions = sh.max_num_partitions;
     p.num_work = sh.num_seqs * sh.num_kv_heads * pl.head_groups * sh.max_num_partitions;
+    p.compact = pl.phase1_compact;
     p.head_stride = (int64_t)sh.head_size * sh.block_size * elem_bytes(sh.kvdt);
     p.blk_stride = p.head_stride * sh.num_kv_heads;
     p.scale_log2 = scale * k_scale * 1.4426950408889634f;

@@ -49,6 +49,7 @@ struct Phase1Params {
     int max_blocks_per_seq;
     int max_num_partitions;
     int num_work;                  // S * KVH * head_groups * maxP
+    int compact;                   // 1: compact schedule over used partitions only
     int64_t blk_stride;            // bytes per physical block (all kv heads)
     int64_t head_stride;           // bytes per (block, kv head)
     float scale_log2;              // scale * k_scale * log2(e)
@@ -90,13 +91,31 @@ constexpr int kPhase1Occupancy = PAV2_PHASE1_OCCUPANCY;
 constexpr bool kPhase1NonTemporal = PAV2_PHASE1_NONTEMPORAL != 0;
 constexpr int kPhase2Threads = 256;
 
-inline int phase1_lds_bytes(int gqa, int head_size, int waves, int bs_log2) {
+// Phase-1 schedule: 0 dense grid, 1 compact list of used partitions, 2 choose
+// (compact for batches of 2 .. kMaxCompactSeqs sequences).
+#ifndef PAV2_PHASE1_SCHEDULE
+#define PAV2_PHASE1_SCHEDULE 2
+#endif
+constexpr int kMaxCompactSeqs = 8192;
+#ifndef PAV2_PHASE1_COMPACT_ROUNDS
+#define PAV2_PHASE1_COMPACT_ROUNDS 8
+#endif
+constexpr int kPhase1CompactRounds = PAV2_PHASE1_COMPACT_ROUNDS;
+
+inline bool phase1_compact(int num_seqs) {
+    if (PAV2_PHASE1_SCHEDULE == 0) return false;
+    if (num_seqs > kMaxCompactSeqs) return false;
+    return PAV2_PHASE1_SCHEDULE == 1 || num_seqs > 1;
+}
+
+inline int phase1_lds_bytes(int gqa, int head_size, int waves, int bs_log2, int num_seqs, bool compact) {
     int heads = gqa < kMaxHeadsPerGroup ? gqa : kMaxHeadsPerGroup;
     int d16 = (head_size + 15) / 16 * 16;
     int table = (kPartition >> bs_log2) * 4;
     return waves * heads * (d16 + 4) * 4      // per-wave partial outputs
            + 3 * waves * kMaxHeadsPerGroup * 4 // per-wave max and sums
-           + table;                            // the partition's block-table slice
+           + table                             // the partition's block-table slice
+           + (compact ? (num_seqs + 1 + waves) * 4 : 0);   // partition-count prefix
 }
 
 inline int phase2_vec(int odt) { return odt == F32 ? 4 : 8; }

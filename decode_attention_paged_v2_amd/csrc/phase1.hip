@@ -150,7 +150,7 @@ __device__ __forceinline__ T load_stream(const uint8_t *p) {
         return *reinterpret_cast<const T *>(p);
 }
 
-template <int QDT, int KVDT, int D, int WAVES>
+template <int QDT, int KVDT, int D, int WAVES, bool COMPACT>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(kPhase1Occupancy)))
 phase1_kernel(const Phase1Params P) {
     using S = Shape<QDT, KVDT, D>;
@@ -162,47 +162,123 @@ phase1_kernel(const Phase1Params P) {
 
     extern __shared__ __align__(16) uint8_t smem[];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wv = tid >> 6;
-    const int col = lane & 15;   // token row (K^T loads), head column (outputs), head-dim row (V^T loads)
-    const int grp = lane >> 4;   // 4-element slice index within the MFMA operand
-
-    // Work item; consecutive items land on the same XCD (blockIdx.x % 8).
-    const int nblk = gridDim.x;
-    int work = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    if (work >= P.num_work) return;
-    const int hg = work % P.head_groups;
-    work /= P.head_groups;
-    const int g = work % P.num_kv_heads;
-    work /= P.num_kv_heads;
-    const int s = work % P.num_seqs;
-    const int p = work / P.num_seqs;
+    const int tid0 = threadIdx.x;
 
     const int maxP = P.max_num_partitions;
-    const int L = P.seq_lens[s];
-    const int start = p * kPartition;
-    const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
-    const int nh = min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
-
-    if (start >= L) {   // unused partition slot
-        if (tid < nh) {
-            const int64_t i = ((int64_t)s * P.num_heads + h0 + tid) * maxP + p;
-            P.max_logits[i] = -INFINITY;
-            P.exp_sums[i] = 0.0f;
-        }
-        return;
-    }
-    const int n_tok = min(kPartition, L - start);
-    const int last = start + n_tok - 1;   // ALiBi reference position: the partition's last token
-
-    // LDS: per-wave partial outputs, per-wave max/sum, block-table slice.
+    const int HG = P.head_groups;
+    const int KVH = P.num_kv_heads;
     const int heads_alloc = min(P.gqa, kMaxHeadsPerGroup);
+    // LDS: per-wave partial outputs, per-wave max/sums, the partition's
+    // block-table slice, then (compact schedule) the partition-count prefix.
     float *s_o = reinterpret_cast<float *>(smem);
     float *s_m = s_o + WAVES * heads_alloc * (S::kD16 + 4);
     float *s_l = s_m + WAVES * kMaxHeadsPerGroup;
     float *s_lr = s_l + WAVES * kMaxHeadsPerGroup;
     int *s_bt = reinterpret_cast<int *>(s_lr + WAVES * kMaxHeadsPerGroup);
+    int *s_pref = s_bt + (kPartition >> P.bs_log2);     // [num_seqs + 1]
+    int *s_wsum = s_pref + P.num_seqs + 1;              // [WAVES]
+
+    // Work items.  Dense schedule: one (partition, seq, kv head, head group)
+    // slot per workgroup, consecutive slots on one XCD (blockIdx.x % 8).
+    // Compact schedule: the workgroup computes the exclusive prefix of the
+    // sequences' partition counts from seq_lens in LDS and takes a contiguous
+    // range of the list of used (seq, partition, kv head, head group) items.
+    int item, item_end;
+    if constexpr (COMPACT) {
+        const int tid = tid0, lane = tid0 & 63, wv = tid0 >> 6;
+        const int nthr = WAVES * 64;
+        const int per_t = (P.num_seqs + nthr - 1) / nthr;
+        auto parts_of = [&](int sq) {
+            const int n = (P.seq_lens[sq] + kPartition - 1) / kPartition;
+            return n < maxP ? (n > 0 ? n : 0) : maxP;
+        };
+        int local = 0;
+        for (int k = 0; k < per_t; ++k) {
+            const int sq = tid * per_t + k;
+            if (sq < P.num_seqs) local += parts_of(sq);
+        }
+        int incl = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        if (lane == 63) s_wsum[wv] = incl;
+        __syncthreads();
+        int run = incl - local, total = 0;
+        for (int w2 = 0; w2 < WAVES; ++w2) {
+            if (w2 < wv) run += s_wsum[w2];
+            total += s_wsum[w2];
+        }
+        for (int k = 0; k < per_t; ++k) {
+            const int sq = tid * per_t + k;
+            if (sq < P.num_seqs) {
+                s_pref[sq] = run;
+                run += parts_of(sq);
+            }
+        }
+        if (tid == 0) s_pref[P.num_seqs] = total;
+        __syncthreads();
+        const int64_t n_items = (int64_t)total * KVH * HG;
+        item = (int)(n_items * blockIdx.x / gridDim.x);            // balanced contiguous ranges
+        item_end = (int)(n_items * (blockIdx.x + 1) / gridDim.x);
+    } else {
+        const int nblk = gridDim.x;
+        item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+        if (item >= P.num_work) return;
+        item_end = item + 1;
+    }
+
+    for (; item < item_end; ++item) {
+    int hg = item % HG;
+    int s, g, p;
+    if constexpr (COMPACT) {
+        int r = item / HG;
+        g = r % KVH;
+        r /= KVH;
+        int lo = 0, hi = P.num_seqs;   // last sequence with prefix <= r
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pref[mid] <= r) lo = mid;
+            else hi = mid;
+        }
+        s = lo;
+        p = r - s_pref[lo];
+    } else {
+        int w = item / HG;
+        g = w % KVH;
+        w /= KVH;
+        s = w % P.num_seqs;
+        p = w / P.num_seqs;
+    }
+    if constexpr (COMPACT) __syncthreads();   // the previous item's LDS is free
+
+    // Lane indices.  In the item loop they are taken from an opaque per-item
+    // copy of the thread id, so that lane-derived address terms are recomputed
+    // per item rather than hoisted out of the loop and kept live across it.
+    int tid = tid0;
+    if constexpr (COMPACT) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int col = lane & 15;   // token row (K^T loads), head column (outputs), head-dim row (V^T loads)
+    const int grp = lane >> 4;   // 4-element slice index within the MFMA operand
+
+    const int L = P.seq_lens[s];
+    const int start = p * kPartition;
+    const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
+    const int nh = min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
+
+    if (start >= L) {   // unused partition slot (dense schedule only)
+        if (tid < nh) {
+            const int64_t i = ((int64_t)s * P.num_heads + h0 + tid) * maxP + p;
+            P.max_logits[i] = -INFINITY;
+            P.exp_sums[i] = 0.0f;
+        }
+        if constexpr (COMPACT) continue;
+        else return;
+    }
+    const int n_tok = min(kPartition, L - start);
+    const int last = start + n_tok - 1;   // ALiBi reference position: the partition's last token
 
     const int bs_log2 = P.bs_log2;
     const int bs_mask = (1 << bs_log2) - 1;
@@ -566,18 +642,62 @@ phase1_kernel(const Phase1Params P) {
             P.exp_sums[srow * maxP + p] = l;
         }
     }
+        if constexpr (!COMPACT) break;
+    }   // item loop
+
+    if constexpr (COMPACT) {   // unused slots p >= P_s of this workgroup's share of sequences
+        for (int sq = blockIdx.x; sq < P.num_seqs; sq += gridDim.x) {
+            const int used = s_pref[sq + 1] - s_pref[sq];
+            const int spare = maxP - used;
+            const int n = P.num_heads * spare;
+            for (int idx = tid0; idx < n; idx += WAVES * 64) {
+                const int h = idx / spare;
+                const int64_t i = ((int64_t)sq * P.num_heads + h) * maxP + used + (idx - h * spare);
+                P.max_logits[i] = -INFINITY;
+                P.exp_sums[i] = 0.0f;
+            }
+        }
+    }
+}
+
+int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <int QDT, int KVDT, int D, bool COMPACT>
+hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
+    constexpr int WAVES = kPhase1Waves;
+    const void *fn = reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, COMPACT>);
+    if (lds > 65536) hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    int grid = (p.num_work + 7) / 8 * 8;
+    if (COMPACT) {
+        // at most kPhase1CompactRounds resident rounds of workgroups, each
+        // walking a balanced range of the used items
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, WAVES * 64, lds) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        const int cap = kPhase1CompactRounds * device_cu_count() * per_cu;
+        grid = grid < cap ? grid : cap;
+    }
+    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, COMPACT>), dim3(grid), dim3(WAVES * 64), lds,
+                       stream, p);
+    return hipGetLastError();
 }
 
 template <int QDT, int KVDT, int D>
 hipError_t launch_one(const Phase1Params &p, int lds, hipStream_t stream) {
-    constexpr int WAVES = kPhase1Waves;
-    const int grid = (p.num_work + 7) / 8 * 8;
-    if (lds > 65536)
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES>), dim3(grid), dim3(WAVES * 64),
-                       lds, stream, p);
-    return hipGetLastError();
+    return p.compact ? launch_sched<QDT, KVDT, D, true>(p, lds, stream)
+                     : launch_sched<QDT, KVDT, D, false>(p, lds, stream);
 }
 
 template <int QDT, int KVDT>

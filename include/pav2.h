@@ -149,6 +149,8 @@ typedef struct {
     int phase2_workgroups;
     int phase2_threads;
     int phase2_lds_bytes;
+    int phase1_compact;       /* 1: phase 1 walks a compact list of used partitions
+                                 (grid: min(phase1_workgroups, 8 resident rounds)) */
 } pav2_plan_t;
 
 int pav2_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size,

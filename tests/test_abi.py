@@ -128,6 +128,7 @@ def test_plan(cfg, expect):
     for k, v in expect.items():
         assert p[k] == v, (k, p)
     assert p["phase1_threads"] == 256 and p["phase2_threads"] == 256
+    assert p["phase1_compact"] == (1 if cfg["num_seqs"] > 1 else 0)
     assert 0 < p["phase1_lds_bytes"] <= 160 * 1024
     assert 0 < p["phase2_lds_bytes"] <= 160 * 1024
 

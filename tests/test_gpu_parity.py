@@ -327,6 +327,23 @@ def test_spare_partition_slots_and_inflated_max_seq_len():
     compare(wl, g, run_oracle(wl))
 
 
+def test_single_sequence_dense_schedule_with_spare_slots():
+    """One sequence runs on the dense grid (one workgroup per partition slot);
+    an inflated max_seq_len makes most slots start past the sequence end."""
+    spec = W.Spec("single", 16, 2, 128, 16, "bf16", "bf16", lambda g: [1300], pool=lambda n: n + 3,
+                  alibi=True, seed=9)
+    wl = W.generate(spec, poison=True)
+    plan = pav2.plan(1, 16, 2, 128, 16, 20, pav2.BF16, pav2.BF16)
+    assert plan["phase1_compact"] == 0
+    wl.max_seq_len = 10000
+    wl.max_num_partitions = 20
+    pad = torch.full((1, 625), -1, dtype=torch.int32)
+    pad[:, :wl.block_tables.shape[1]] = wl.block_tables
+    wl.block_tables = pad
+    g = run_gpu(wl.to(DEV))
+    compare(wl, g, run_oracle(wl))
+
+
 def test_split_phases_match_single_call_and_are_deterministic():
     wl = W.generate(W.SMALL_SPECS["ragged_alibi"], poison=True).to(DEV)
     a = run_gpu(wl)
