@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from decode_attention_paged_v2_amd import workloads as W  # noqa: E402
+from decode_attention_paged_v2_amd import accounting  # noqa: E402
 import decode_attention_paged_v2_amd as pav2  # noqa: E402
 
 DESCR = {
@@ -43,30 +44,6 @@ DESCR = {
     "fp8_kv": "64 seqs x 16384 tokens, H=64, kv_h=8, d=128, e4m3 KV (k_scale 0.05, v_scale 0.04), bf16 q/out, block 32",
 }
 DTYPE_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
-
-
-def phase1_bytes(wl) -> int:
-    """Algorithmic HBM bytes of one phase-1 launch.
-
-    K and V of every cached token once per kv head (2 * d * b_kv per
-    (token, kv head)), the query, the block-table entries the sequences use,
-    and the per-partition outputs written: tmp_output rows plus max_logits and
-    exp_sums (4 bytes each) for every (seq, head, partition) slot.
-    """
-    qb = wl.query.element_size()
-    S, H, D, P = wl.num_seqs, wl.num_heads, wl.head_size, wl.max_num_partitions
-    used_parts = sum((L + 511) // 512 for L in wl.seq_lens_host)
-    blocks = sum((L + wl.block_size - 1) // wl.block_size for L in wl.seq_lens_host)
-    return (wl.kv_bytes() + S * H * D * qb + 4 * blocks
-            + used_parts * H * D * qb + 2 * 4 * S * H * P)
-
-
-def phase2_bytes(wl) -> int:
-    """Algorithmic bytes of phase 2: read the used partition rows and stats, write output."""
-    qb = wl.query.element_size()
-    S, H, D = wl.num_seqs, wl.num_heads, wl.head_size
-    used_parts = sum((L + 511) // 512 for L in wl.seq_lens_host)
-    return used_parts * H * (D * qb + 8) + S * H * D * qb + 4 * S
 
 
 def cpu_baseline(wl, out_gpu, target_core_seconds=15.0, max_threads=16):
@@ -110,6 +87,21 @@ def cpu_baseline(wl, out_gpu, target_core_seconds=15.0, max_threads=16):
         "seconds": round(dt, 3),
         "parity_max_abs_err_vs_gpu": err,
     }
+
+
+def measured_traffic(config):
+    """HBM bytes per phase-1 launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain
+    copy's reading) from the committed counter summary, or None when there is
+    none or it was taken on different kernel sources."""
+    from decode_attention_paged_v2_amd import rocprof_harness
+    path = os.path.join(ROOT, "profiles", f"phase1_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    if data.get("source_hash") != rocprof_harness.source_hash() or "phase1_traffic_bytes" not in data:
+        return None
+    return round(float(data["phase1_traffic_bytes"]))
 
 
 def copy_reference(dev, steps, warmup, nbytes=1 << 30):
@@ -211,7 +203,8 @@ def main():
         del scratch
 
     kv = wl.kv_bytes()
-    b1 = phase1_bytes(wl)
+    b1 = accounting.workload_bytes(wl)["phase1"]
+    traffic = measured_traffic(args.config)
     p1_mean = float(np.mean(p1_ms))
     achieved = b1 / (p1_mean * 1e-3) / 1e9
     value = kv / (ms_per_step * 1e-3) / 1e9
@@ -240,7 +233,8 @@ def main():
         "phase2_plus_gap_ms": round(ms_per_step - p1_mean, 5),
         "cold_cache_step_ms_median": round(float(np.median(cold)), 5) if cold else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
                      "kernel": "phase1_kernel", "algorithmic_bytes_per_launch": b1},
         "generate_s": round(gen_s, 2),
         "library": pav2.lib_path(),

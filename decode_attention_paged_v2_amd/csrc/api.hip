@@ -122,8 +122,11 @@ void make_plan(const Shape &s, pav2_plan_t *pl) {
     pl->phase1_lds_bytes =
         pav2::phase1_lds_bytes(gqa, s.head_size, pav2::kPhase1Waves, bs_log2, s.num_seqs, compact);
     pl->phase1_compact = compact ? 1 : 0;
-    pl->phase2_workgroups = s.num_seqs * s.num_heads;
-    pl->phase2_threads = pav2::kPhase2Threads;
+    pl->phase2_workgroups = pav2::phase2_workgroups((int64_t)s.num_seqs * s.num_heads, s.max_num_partitions);
+    {
+        const int wpp = pav2::phase2_waves_per_pair(s.max_num_partitions);
+        pl->phase2_threads = 64 * (wpp > 4 ? wpp : 4);
+    }
     pl->phase2_lds_bytes = pav2::phase2_lds_bytes(s.max_num_partitions, s.head_size, s.qdt);
 }
 

@@ -121,9 +121,21 @@ inline int phase1_lds_bytes(int gqa, int head_size, int waves, int bs_log2, int 
 inline int phase2_vec(int odt) { return odt == F32 ? 4 : 8; }
 
 inline int phase2_lds_bytes(int max_num_partitions, int head_size, int odt) {
-    int vec = phase2_vec(odt);
-    int rows = kPhase2Threads / (head_size / vec);
-    return max_num_partitions * 4 + rows * head_size * 4 + 64 * 4;
+    (void)max_num_partitions, (void)head_size, (void)odt;
+    return 0;   // phase 2 keeps everything in registers
+}
+
+// Wavefronts phase 2 gives one (sequence, head): one for up to 64 partition
+// slots (a workgroup serves four pairs), 4 up to 128, 16 beyond (one
+// workgroup of that many wavefronts per pair).
+inline int phase2_waves_per_pair(int max_num_partitions) {
+    return max_num_partitions > 128 ? 16 : (max_num_partitions > 64 ? 4 : 1);
+}
+
+inline int phase2_workgroups(int64_t pairs, int max_num_partitions) {
+    const int wpp = phase2_waves_per_pair(max_num_partitions);
+    const int wg_waves = wpp > 4 ? wpp : 4;
+    return (int)((pairs * wpp + wg_waves - 1) / wg_waves);
 }
 
 }  // namespace pav2

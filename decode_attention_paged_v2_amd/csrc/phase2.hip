@@ -8,10 +8,8 @@
 // reduce would divide 0 by 0 there).  There is no cap on the partition count
 // (page 2 truncates past 1024).
 //
-// One workgroup per (sequence, head).  Weights are computed once into LDS;
-// the partitions are then split across thread groups, each thread reading one
-// 16-byte vector of a partition row per step (rows are contiguous in
-// tmp_output), and the groups' partial sums are added through LDS.
+// Short contexts: one wavefront per (sequence, head); long contexts: one
+// 4-wavefront workgroup per (sequence, head).  See phase2_kernel.
 #include <math.h>
 
 #include "pav2_internal.h"
@@ -20,21 +18,6 @@ namespace pav2 {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float block_reduce(float v, float *scratch, bool is_max) {
-    for (int off = 32; off > 0; off >>= 1) {
-        float o = __shfl_xor(v, off);
-        v = is_max ? fmaxf(v, o) : v + o;
-    }
-    const int wv = threadIdx.x >> 6;
-    const int nw = blockDim.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[wv] = v;
-    __syncthreads();
-    v = scratch[0];
-    for (int i = 1; i < nw; ++i) v = is_max ? fmaxf(v, scratch[i]) : v + scratch[i];
-    return v;
-}
 
 template <int ODT>
 __device__ __forceinline__ void load_vec(const uint8_t *src, float (&v)[ODT == F32 ? 4 : 8]) {
@@ -81,116 +64,196 @@ __device__ __forceinline__ void store_vec(uint8_t *dst, const float (&v)[ODT == 
     }
 }
 
-template <int ODT, int D>
-__global__ void __launch_bounds__(kPhase2Threads) phase2_kernel(const Phase2Params P) {
+// Online (max, sum of exp-weighted exp_sums) pair combine.
+__device__ __forceinline__ void lse_merge(float &m, float &w, float m2, float w2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;   // both empty
+    w = w * __builtin_amdgcn_exp2f((m - mn) * kLog2e) + w2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
+    m = mn;
+}
+
+// WPP wavefronts per (sequence, head): 1 for short contexts (a workgroup
+// serves 4 pairs), 4 for long ones (one pair per workgroup).  A wavefront's
+// lanes form G groups of TPR lanes; lane (gi, r) owns VEC consecutive
+// head-dim elements r*VEC.. of the row and the partitions
+// q, q + Q, q + 2Q, ... with q = sub*G + gi and Q = WPP*G groups in all.
+//   1. One pass over the used partitions' statistics gives the global
+//      (max M, sum W of exp(m_p - M) l_p) by an online merge; the first batch
+//      of tmp_output rows is loaded alongside it.
+//   2. Each lane accumulates exp(m_p - M) l_p * o_p over its partitions.
+//   3. Groups are added across lanes, then (WPP = 4) across wavefronts in LDS;
+//      the row is scaled by 1 / W and stored.
+template <int ODT, int D, int WPP>
+__global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const Phase2Params P) {
     constexpr int VEC = ODT == F32 ? 4 : 8;
     constexpr int EB = ODT == F32 ? 4 : 2;
-    constexpr int TPR = D / VEC;                    // threads per partition row
-    constexpr int G = kPhase2Threads / TPR;         // partition groups
-    extern __shared__ __align__(16) float sm[];
+    constexpr int TPR = D / VEC;                    // lanes per row
+    constexpr int G = 64 / TPR;                     // partition groups per wavefront
+    constexpr int Q = WPP * G;                      // partition groups per pair
+    constexpr int B = WPP == 4 ? 16 : 8;            // rows in flight per lane
+    constexpr int WG_WAVES = WPP > 4 ? WPP : 4;
+    static_assert(D % VEC == 0 && TPR <= 64, "row split");
+    __shared__ float red[WPP > 1 ? WPP * D : 1];
 
-    const int maxP = P.max_num_partitions;
-    float *s_w = sm;                                // [maxP] combine weights
-    float *s_red = sm + maxP;                       // [G][D] partial sums
-    float *s_misc = s_red + G * D;                  // [64] reduction scratch
-
-    const int tid = threadIdx.x;
-    const int64_t sh = blockIdx.x;                  // s * H + h
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t gw = (int64_t)blockIdx.x * WG_WAVES + wv;
+    const int64_t sh = gw / WPP;                    // s * H + h
+    const int sub = (int)(gw % WPP);
+    if (sh >= (int64_t)P.num_seqs * P.num_heads) return;   // uniform per workgroup when WPP > 1
     const int s = (int)(sh / P.num_heads);
+    const int maxP = P.max_num_partitions;
     const int L = P.seq_lens[s];
     int np = (L + kPartition - 1) / kPartition;
     np = np < maxP ? np : maxP;
-    uint8_t *out = reinterpret_cast<uint8_t *>(P.out) + sh * D * EB;
+    const int gi = lane / TPR;
+    const int r = lane - gi * TPR;
+    const bool active = gi < G;
+    const int q = sub * G + gi;
+    uint8_t *out = reinterpret_cast<uint8_t *>(P.out) + (sh * D + r * VEC) * EB;
 
     if (L <= 0) {
-        if (tid < TPR) {
+        if (sub == 0 && gi == 0) {
             float z[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) z[e] = 0.0f;
-            store_vec<ODT>(out + tid * VEC * EB, z);
+            store_vec<ODT>(out, z);
         }
         return;
     }
 
     const float *ml = P.max_logits + sh * maxP;
     const float *es = P.exp_sums + sh * maxP;
-    float mx = -INFINITY;
-    for (int p = tid; p < np; p += kPhase2Threads) mx = fmaxf(mx, ml[p]);
-    const float M = block_reduce(mx, s_misc, true);
-    float ws = 0.0f;
-    for (int p = tid; p < np; p += kPhase2Threads) {
-        const float w = __builtin_amdgcn_exp2f((ml[p] - M) * kLog2e) * es[p];
-        s_w[p] = w;
-        ws += w;
-    }
-    const float W = block_reduce(ws, s_misc + 8, false);   // its barriers publish s_w
+    const uint8_t *src = reinterpret_cast<const uint8_t *>(P.tmp_out) + (sh * maxP * D + r * VEC) * EB;
 
-    const int r = tid % TPR;
-    const int gi = tid / TPR;
+    // A batch: B rows of this lane with their statistics, loaded together.
+    float v[B][VEC], bm[B], be[B];
+    auto load_batch = [&](int p0) {
+#pragma unroll
+        for (int k = 0; k < B; ++k) {
+            const int p = p0 + k * Q;
+            bm[k] = -INFINITY;
+            be[k] = 0.0f;
+            if (active && p < np) {
+                load_vec<ODT>(src + (int64_t)p * D * EB, v[k]);
+                bm[k] = ml[p];
+                be[k] = es[p];
+            }
+        }
+    };
+    load_batch(q);   // the first batch is in flight during the statistics pass
+
+    float m = -INFINITY, w = 0.0f;
+    for (int p0 = lane; p0 < np; p0 += 4 * 64) {
+        float sm[4], se[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int p = p0 + k * 64;
+            sm[k] = p < np ? ml[p] : -INFINITY;
+            se[k] = p < np ? es[p] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lse_merge(m, w, sm[k], se[k]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(m, off), w2 = __shfl_xor(w, off);
+        lse_merge(m, w, m2, w2);
+    }
+
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
-    if (gi < G) {
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(P.tmp_out) +
-                             (sh * maxP * D + r * VEC) * EB;
-        int p = gi;
-        for (; p + 3 * G < np; p += 4 * G) {
-            float v0[VEC], v1[VEC], v2[VEC], v3[VEC];
-            load_vec<ODT>(src + (int64_t)p * D * EB, v0);
-            load_vec<ODT>(src + (int64_t)(p + G) * D * EB, v1);
-            load_vec<ODT>(src + (int64_t)(p + 2 * G) * D * EB, v2);
-            load_vec<ODT>(src + (int64_t)(p + 3 * G) * D * EB, v3);
-            const float w0 = s_w[p], w1 = s_w[p + G], w2 = s_w[p + 2 * G], w3 = s_w[p + 3 * G];
+    auto add_batch = [&]() {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] += w0 * v0[e] + w1 * v1[e] + w2 * v2[e] + w3 * v3[e];
+        for (int k = 0; k < B; ++k) {
+            if (be[k] != 0.0f) {   // rows past np (and inactive lanes) carry be = 0
+                const float wp = __builtin_amdgcn_exp2f((bm[k] - m) * kLog2e) * be[k];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] += wp * v[k][e];
+            }
         }
-        for (; p < np; p += G) {
-            float v0[VEC];
-            load_vec<ODT>(src + (int64_t)p * D * EB, v0);
-            const float w0 = s_w[p];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] += w0 * v0[e];
-        }
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) s_red[gi * D + r * VEC + e] = acc[e];
+    };
+    add_batch();
+    for (int p0 = q + B * Q; p0 < np; p0 += B * Q) {
+        load_batch(p0);
+        add_batch();
     }
-    __syncthreads();
-    if (tid < TPR) {
-        float v[VEC];
-        const float inv = 1.0f / W;
+    // add the G groups of the wavefront (lanes r, r + TPR, ...)
+    if constexpr ((G & (G - 1)) == 0 && G * TPR == 64) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            float a = 0.0f;
-            for (int k = 0; k < G; ++k) a += s_red[k * D + tid * VEC + e];
-            v[e] = a * inv;
+        for (int off = TPR; off < 64; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+    } else {
+        float t[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) t[e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) t[e] += __shfl(acc[e], r + k * TPR);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = t[e];
+    }
+    if constexpr (WPP > 1) {
+        if (gi == 0) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) red[sub * D + r * VEC + e] = acc[e];
         }
-        store_vec<ODT>(out + tid * VEC * EB, v);
+        __syncthreads();
+        if (sub != 0) return;
+        if (gi == 0) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float a = 0.0f;
+#pragma unroll
+                for (int k = 0; k < WPP; ++k) a += red[k * D + r * VEC + e];
+                acc[e] = a;
+            }
+        }
+    }
+    if (gi == 0) {
+        const float inv = 1.0f / w;
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = acc[e] * inv;
+        store_vec<ODT>(out, o);
+    }
+}
+
+template <int ODT, int D, int WPP>
+hipError_t launch_wpp(const Phase2Params &p, hipStream_t stream) {
+    constexpr int WG_WAVES = WPP > 4 ? WPP : 4;
+    const int64_t waves = (int64_t)p.num_seqs * p.num_heads * WPP;
+    const dim3 grid((unsigned)((waves + WG_WAVES - 1) / WG_WAVES));
+    hipLaunchKernelGGL((phase2_kernel<ODT, D, WPP>), grid, dim3(64 * WG_WAVES), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int ODT, int D>
+hipError_t launch_one(const Phase2Params &p, hipStream_t stream) {
+    switch (phase2_waves_per_pair(p.max_num_partitions)) {
+    case 16: return launch_wpp<ODT, D, 16>(p, stream);
+    case 4: return launch_wpp<ODT, D, 4>(p, stream);
+    default: return launch_wpp<ODT, D, 1>(p, stream);
     }
 }
 
 template <int ODT>
 hipError_t launch_d(const Phase2Params &p, int D, int lds, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_heads));
-    const dim3 block(kPhase2Threads);
-#define PAV2_P2(DD)                                                                        \
-    case DD:                                                                               \
-        if (lds > 65536)                                                                   \
-            hipFuncSetAttribute(reinterpret_cast<const void *>(&phase2_kernel<ODT, DD>),   \
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);          \
-        hipLaunchKernelGGL((phase2_kernel<ODT, DD>), grid, block, lds, stream, p);         \
-        return hipGetLastError();
+    (void)lds;
     switch (D) {
-        PAV2_P2(64)
-        PAV2_P2(80)
-        PAV2_P2(96)
-        PAV2_P2(112)
-        PAV2_P2(120)
-        PAV2_P2(128)
-        PAV2_P2(192)
-        PAV2_P2(256)
+    case 64: return launch_one<ODT, 64>(p, stream);
+    case 80: return launch_one<ODT, 80>(p, stream);
+    case 96: return launch_one<ODT, 96>(p, stream);
+    case 112: return launch_one<ODT, 112>(p, stream);
+    case 120: return launch_one<ODT, 120>(p, stream);
+    case 128: return launch_one<ODT, 128>(p, stream);
+    case 192: return launch_one<ODT, 192>(p, stream);
+    case 256: return launch_one<ODT, 256>(p, stream);
     default: return hipErrorInvalidValue;
     }
-#undef PAV2_P2
 }
 
 // ---- device-side decoding of KV elements (test hook) -------------------------

@@ -1,0 +1,202 @@
+"""rocprofv3 harness: per-kernel durations and HBM traffic of the decode path.
+
+    python -m decode_attention_paged_v2_amd.rocprof_harness --config long_gqa \
+        --out gpurun_out/prof [--pmc]
+
+Runs `bench.py` (a few steps, no CPU baseline) under
+
+* `rocprofv3 --kernel-trace --stats` -> average / min / max duration of the
+  phase-1 and phase-2 kernels;
+* with `--pmc`, two counter passes (`FETCH_SIZE`, then `WRITE_SIZE`, KiB per
+  dispatch) over the same command and over `bench.py --mode copy` (a plain
+  1 GiB copy).  Each counter is scaled by the ratio of the copy's known bytes
+  to what the counter reports for it, giving HBM bytes per phase-1 launch.
+
+Writes `<out>/<kernel>_<config>.md` (a short summary with the commands) and
+`<out>/<kernel>_<config>.json` (the numbers, plus a hash of the kernel sources
+so that bench.py can tell whether the counters still describe the current
+kernel).  rocprofv3 runs as a child process from /tmp with TMPDIR=/tmp; this
+module never touches the GPU itself.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import shutil
+import subprocess
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+BENCH = os.path.join(ROOT, "bench.py")
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("phase1.hip", "phase2.hip", "pav2_internal.h")]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _run(cmd, log, timeout):
+    env = dict(os.environ, TMPDIR="/tmp")
+    print("[harness] " + " ".join(cmd), flush=True)
+    with open(log, "w") as fh:
+        p = subprocess.Popen(cmd, stdout=fh, stderr=subprocess.STDOUT, cwd="/tmp", env=env,
+                             start_new_session=True)
+        try:
+            rc = p.wait(timeout=timeout)
+        except subprocess.TimeoutExpired:
+            os.killpg(p.pid, 9)
+            p.wait()
+            raise RuntimeError(f"timed out: {' '.join(cmd)}")
+    if rc != 0:
+        with open(log) as fh:
+            tail = fh.read()[-2000:]
+        raise RuntimeError(f"rc={rc}: {' '.join(cmd)}\n{tail}")
+
+
+def _csv(pattern):
+    files = glob.glob(pattern, recursive=True)
+    if not files:
+        raise RuntimeError(f"no file matches {pattern}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _kind(name: str) -> str:
+    if "phase1_kernel" in name:
+        return "phase1"
+    if "phase2_kernel" in name:
+        return "phase2"
+    return "other"
+
+
+def kernel_trace(config: str, out: str, steps: int = 10) -> dict:
+    d = os.path.join(out, f"trace_{config}")
+    shutil.rmtree(d, ignore_errors=True)
+    bench = [sys.executable, BENCH, "--config", config, "--steps", str(steps), "--warmup", "2",
+             "--no-cpu-baseline", "--flush-steps", "0"]
+    cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", d, "-o", "run", "--output-format", "csv",
+           "--"] + bench
+    _run(cmd, os.path.join(out, f"trace_{config}.log"), 300)
+    rel = os.path.relpath(d, ROOT)
+    res = {"command": " ".join(["rocprofv3", "--kernel-trace", "--stats", "-d", rel, "-o", "run",
+                                "--output-format", "csv", "--", "python3", "bench.py"] + bench[2:])}
+    for r in _csv(os.path.join(d, "**", "run_kernel_stats.csv")):
+        k = _kind(r["Name"])
+        if k == "other":
+            continue
+        res[k] = {"name": r["Name"], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                  "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+    return res
+
+
+def pmc(config: str, out: str) -> dict:
+    """FETCH_SIZE and WRITE_SIZE per phase-1 launch, scaled by the copy reference."""
+    res = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        for what in (config, "copy"):
+            d = os.path.join(out, f"pmc_{counter}_{what}")
+            shutil.rmtree(d, ignore_errors=True)
+            if what == "copy":
+                bench = [sys.executable, BENCH, "--mode", "copy", "--steps", "3", "--warmup", "1"]
+            else:
+                bench = [sys.executable, BENCH, "--config", what, "--steps", "3", "--warmup", "1",
+                         "--no-cpu-baseline", "--flush-steps", "0"]
+            cmd = ["rocprofv3", "--pmc", counter, "-d", d, "-o", "run", "--output-format", "csv",
+                   "--"] + bench
+            _run(cmd, os.path.join(out, f"pmc_{counter}_{what}.log"), 120)
+            rows = _csv(os.path.join(d, "**", "run_counter_collection.csv"))
+            if what == "copy":
+                vals = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+                # the reference copy moves 1 GiB each way
+                res[f"{counter}_copy_kib"] = sum(vals) / len(vals)
+                res[f"{counter}_scale"] = (1 << 30) / 1024.0 / res[f"{counter}_copy_kib"]
+            else:
+                for k in ("phase1", "phase2"):
+                    vals = [float(r["Counter_Value"]) for r in rows if _kind(r["Kernel_Name"]) == k]
+                    res[f"{counter}_{k}_kib"] = sum(vals) / len(vals)
+    for k in ("phase1", "phase2"):
+        res[f"{k}_fetch_bytes"] = res[f"FETCH_SIZE_{k}_kib"] * 1024 * res["FETCH_SIZE_scale"]
+        res[f"{k}_write_bytes"] = res[f"WRITE_SIZE_{k}_kib"] * 1024 * res["WRITE_SIZE_scale"]
+    return res
+
+
+def algorithmic_bytes(config: str) -> dict:
+    """Phase-1 / phase-2 algorithmic bytes of the workload (host-side, no GPU)."""
+    from . import accounting, workloads
+    return accounting.spec_bytes(workloads.SPECS[config])
+
+
+def write_summary(config: str, out: str, trace: dict, counters: dict | None) -> str:
+    alg = algorithmic_bytes(config)
+    p1 = trace["phase1"]
+    name = "phase1_" + config
+    lines = [f"# Phase 1 / phase 2 profile: {config}", "",
+             f"Kernel sources hash: `{source_hash()}`", "",
+             "Kernel trace command (from the repository root):", "",
+             "    python -m decode_attention_paged_v2_amd.rocprof_harness --config "
+             f"{config} --out gpurun_out/prof{' --pmc' if counters else ''}", "",
+             "which runs:", "", "    " + trace["command"], "",
+             "| kernel | calls | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|"]
+    for k in ("phase1", "phase2"):
+        t = trace.get(k)
+        if t:
+            lines.append(f"| `{t['name'][:90]}` | {t['calls']} | {t['avg_us']:.2f} | {t['min_us']:.2f} | "
+                         f"{t['max_us']:.2f} |")
+    gbps = alg["phase1"] / (p1["avg_us"] * 1e-6) / 1e9
+    lines += ["", f"Phase-1 algorithmic bytes per launch: {alg['phase1']:,} "
+                  f"(K/V {alg['kv']:,}); at the average duration that is {gbps:.1f} GB/s = "
+                  f"{100 * gbps / 8000:.1f} % of 8 TB/s."]
+    data = {"config": config, "source_hash": source_hash(), "trace": trace, "algorithmic": alg,
+            "phase1_achieved_GBps": gbps, "taken": time.strftime("%Y-%m-%d %H:%M:%S")}
+    if counters:
+        f1, w1 = counters["phase1_fetch_bytes"], counters["phase1_write_bytes"]
+        data["counters"] = counters
+        data["phase1_traffic_bytes"] = f1 + w1
+        lines += ["", "HBM counters (`rocprofv3 --pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, each over "
+                      "the same bench command and over `bench.py --mode copy`, a 1 GiB copy):", "",
+                  "| quantity | value |", "|---|---|",
+                  f"| FETCH_SIZE of the 1 GiB copy (KiB) | {counters['FETCH_SIZE_copy_kib']:.1f} |",
+                  f"| WRITE_SIZE of the 1 GiB copy (KiB) | {counters['WRITE_SIZE_copy_kib']:.1f} |",
+                  f"| scale factors (known / counted) | fetch {counters['FETCH_SIZE_scale']:.4f}, "
+                  f"write {counters['WRITE_SIZE_scale']:.4f} |",
+                  f"| phase-1 FETCH_SIZE per launch (KiB, raw) | {counters['FETCH_SIZE_phase1_kib']:.1f} |",
+                  f"| phase-1 WRITE_SIZE per launch (KiB, raw) | {counters['WRITE_SIZE_phase1_kib']:.1f} |",
+                  f"| phase-1 HBM read bytes (scaled) | {f1:,.0f} |",
+                  f"| phase-1 HBM write bytes (scaled) | {w1:,.0f} |",
+                  f"| algorithmic reads / writes | {alg['phase1_read']:,} / {alg['phase1_write']:,} |",
+                  f"| measured / algorithmic | reads {f1 / alg['phase1_read']:.4f}, "
+                  f"writes {w1 / alg['phase1_write']:.4f} |"]
+    with open(os.path.join(out, name + ".md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    with open(os.path.join(out, name + ".json"), "w") as fh:
+        json.dump(data, fh, indent=1)
+    return os.path.join(out, name + ".md")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--config", default="long_gqa")
+    ap.add_argument("--out", default="gpurun_out/prof")
+    ap.add_argument("--pmc", action="store_true")
+    ap.add_argument("--steps", type=int, default=10)
+    a = ap.parse_args()
+    out = os.path.abspath(a.out)
+    os.makedirs(out, exist_ok=True)
+    trace = kernel_trace(a.config, out, a.steps)
+    counters = pmc(a.config, out) if a.pmc else None
+    path = write_summary(a.config, out, trace, counters)
+    print(open(path).read(), flush=True)
+
+
+if __name__ == "__main__":
+    main()
