@@ -63,7 +63,11 @@ def spec_bytes(spec) -> dict:
     qb = W.elem_size(W._DT[spec.q_dtype])
     kvb = W.elem_size(W._DT[spec.kv_dtype])
     maxP = max(1, (max(lens) + PARTITION_SIZE - 1) // PARTITION_SIZE)
+    used_parts = sum((L + PARTITION_SIZE - 1) // PARTITION_SIZE for L in lens)
+    head_groups = -(-(spec.num_heads // spec.num_kv_heads) // 16)
     return {
+        # phase-1 work items: (used partition, kv head, group of <= 16 query heads)
+        "phase1_items": used_parts * spec.num_kv_heads * head_groups,
         "kv": kv_bytes(lens, spec.num_kv_heads, spec.head_size, kvb),
         "phase1": phase1_bytes(lens, spec.num_heads, spec.num_kv_heads, spec.head_size, spec.block_size,
                                qb, kvb, maxP),

@@ -218,6 +218,7 @@ phase1_kernel(const Phase1Params P) {
             }
         }
         if (tid == 0) s_pref[P.num_seqs] = total;
+        total = __builtin_amdgcn_readfirstlane(total);   // wave-uniform: keep the item loop scalar
         __syncthreads();
         const int64_t n_items = (int64_t)total * KVH * HG;
         item = (int)(n_items * blockIdx.x / gridDim.x);            // balanced contiguous ranges
@@ -236,14 +237,14 @@ phase1_kernel(const Phase1Params P) {
         int r = item / HG;
         g = r % KVH;
         r /= KVH;
-        int lo = 0, hi = P.num_seqs;   // last sequence with prefix <= r
+        int lo = 0, hi = P.num_seqs;   // last sequence with prefix <= r (scalar search)
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (s_pref[mid] <= r) lo = mid;
+            if (__builtin_amdgcn_readfirstlane(s_pref[mid]) <= r) lo = mid;
             else hi = mid;
         }
         s = lo;
-        p = r - s_pref[lo];
+        p = r - __builtin_amdgcn_readfirstlane(s_pref[lo]);
     } else {
         int w = item / HG;
         g = w % KVH;
@@ -259,7 +260,7 @@ phase1_kernel(const Phase1Params P) {
     int tid = tid0;
     if constexpr (COMPACT) asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int col = lane & 15;   // token row (K^T loads), head column (outputs), head-dim row (V^T loads)
     const int grp = lane >> 4;   // 4-element slice index within the MFMA operand
 
@@ -310,6 +311,7 @@ phase1_kernel(const Phase1Params P) {
         }
     }
 
+    // ALiBi slope in log2 units (0 without ALiBi, so the bias terms vanish).
     float slope2 = 0.0f;
     if (P.alibi != nullptr && hvalid) slope2 = P.alibi[h0 + col] * kLog2e;
     const float scale_log2 = P.scale_log2;
@@ -426,7 +428,6 @@ phase1_kernel(const Phase1Params P) {
     u32x4 kbuf[PF][KH][NKL];
     Words<VW> vbuf[PF][DPG];
     float sc[UPW][8];                 // scores of the lane's 8 tokens per unit (log2 units)
-    const bool has_alibi = P.alibi != nullptr;
 
     auto issue = [&](int j) {
         if (j < GK) {
@@ -453,13 +454,17 @@ phase1_kernel(const Phase1Params P) {
         for (int hh = 0; hh < KH; ++hh) {
             const int half = (j % KG) * KH + hh;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[u][4 * half + i] = acc[hh][i] * scale_log2;
+            for (int i = 0; i < 4; ++i) sc[u][4 * half + i] = acc[hh][i];
         }
     }
     // Regroup each unit's scores so that lane group g holds tokens 8g .. 8g+7:
     // swapping the upper 32 lanes of the first tile with the lower 32 of the
     // second, then odd 16-lane rows of the first with even rows of the second,
     // leaves tokens 8g + i in the first register and 8g + 4 + i in the second.
+    // Then scale and ALiBi bias (slope * (t - last), the lane's first token of
+    // unit u being t = start + (wv + WAVES u) * 32 + 8 grp); tokens at or past
+    // the sequence end (only in the last unit, or in a clamped one) get -inf.
+    const float bias0 = slope2 * (float)(start + wv * UNIT + 8 * grp - last);
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
 #pragma unroll
@@ -469,14 +474,15 @@ phase1_kernel(const Phase1Params P) {
             sc[u][i] = as_f32(q[0]);
             sc[u][4 + i] = as_f32(q[1]);
         }
-        const int t0 = start + unit_of(u) * UNIT + 8 * grp;   // unclamped
-        const bool partial = start + unit_of(u) * UNIT + UNIT > L;
+        const float bu = u == 0 ? bias0 : fmaf(slope2, (float)(WAVES * UNIT * u), bias0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = sc[u][e];
-            if (has_alibi) v += slope2 * (float)(t0 + e - last);
-            if (partial) v = (t0 + e < L) ? v : -INFINITY;
-            sc[u][e] = v;
+        for (int e = 0; e < 8; ++e)
+            sc[u][e] = fmaf(sc[u][e], scale_log2, e == 0 ? bu : fmaf(slope2, (float)e, bu));
+        const int tu = start + unit_of(u) * UNIT;   // unclamped first token of the unit
+        if (tu + UNIT > L) {
+            const int nv = L - (tu + 8 * grp);      // valid tokens among the lane's 8
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc[u][e] = e < nv ? sc[u][e] : -INFINITY;
         }
     }
 
@@ -492,18 +498,24 @@ phase1_kernel(const Phase1Params P) {
     // exp_sums); lsum_r sums the weights as they enter the MFMAs, so that the
     // partition output is a true weighted mean of V rows.  16-bit operands
     // carry P as hi + lo, two 16-bit parts (~16 significant bits).
+    // The rounded weights' sum comes from one more MFMA pair per unit against
+    // an all-ones A operand (every row of that tile is sum_t P[t][head]).
     float lsum = 0.0f, lsum_r = 0.0f;
     float pr[8];
     u32x4 ph = {0u, 0u, 0u, 0u}, pl = {0u, 0u, 0u, 0u};
-    uint32_t vmask[4] = {~0u, ~0u, ~0u, ~0u};
+    f32x4 osum = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t one2 = pack2<QDT == F32 ? BF16 : QDT>(1.0f, 1.0f);
+    const u32x4 ones = {one2, one2, one2, one2};
+    // Raw-word masks zeroing V of tokens past the sequence end (word w of a
+    // lane's 8-token slice holds tokens w * TPW .. w * TPW + TPW - 1).
+    constexpr int TPW = 4 / KVB;
+    uint32_t vmask[VW];
     bool vpartial = false;
 #pragma unroll
     for (int j = GK; j < NG; ++j) {
         const int u = (j - GK) / VSPLIT;
         const int part = (j - GK) % VSPLIT;
         if (part == 0) {
-            const int t0 = start + unit_of(u) * UNIT + 8 * grp;
-            vpartial = start + unit_of(u) * UNIT + UNIT > L;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 pr[e] = exp2_fast(sc[u][e] - mu);
@@ -515,19 +527,32 @@ phase1_kernel(const Phase1Params P) {
                     const uint32_t h = pack2<QDT>(pr[2 * k], pr[2 * k + 1]);
                     const float r0 = pr[2 * k] - unpack_lo<QDT>(h);
                     const float r1 = pr[2 * k + 1] - unpack_hi<QDT>(h);
-                    const uint32_t l = pack2<QDT>(r0, r1);
                     ph[k] = h;
-                    pl[k] = l;
-                    lsum_r += (unpack_lo<QDT>(h) + unpack_lo<QDT>(l)) + (unpack_hi<QDT>(h) + unpack_hi<QDT>(l));
+                    pl[k] = pack2<QDT>(r0, r1);
                 }
+                osum = mfma_k32<QDT>(ones, ph, osum);
+                osum = mfma_k32<QDT>(ones, pl, osum);
             }
+            const int tu = start + unit_of(u) * UNIT;
+            vpartial = tu + UNIT > L;
             if (vpartial) {
+                const int nv = L - (tu + 8 * grp);
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    vmask[k] = (t0 + 2 * k < L ? 0x0000ffffu : 0u) | (t0 + 2 * k + 1 < L ? 0xffff0000u : 0u);
+                for (int w = 0; w < VW; ++w) {
+                    const int nb = min(max(nv - w * TPW, 0), TPW) * KVB;   // valid bytes of the word
+                    vmask[w] = nb >= 4 ? ~0u : (1u << (8 * nb)) - 1u;
+                }
             }
         }
         Words<VW> (&vr)[DPG] = vbuf[j % PF];
+        if (vpartial) {
+#pragma unroll
+            for (int i = 0; i < DPG; ++i) {
+                if (part * DPG + i >= NDT) break;
+#pragma unroll
+                for (int w = 0; w < VW; ++w) vr[i].w[w] &= vmask[w];
+            }
+        }
 #pragma unroll
         for (int i = 0; i < DPG; ++i) {
             const int dt = part * DPG + i;
@@ -541,12 +566,6 @@ phase1_kernel(const Phase1Params P) {
                     a[3] = fp8x2_to_16<QDT, true>(vr[i].w[1]);
                 } else {
                     a = u32x4{vr[i].w[0], vr[i].w[1], vr[i].w[2], vr[i].w[3]};
-                }
-                if (vpartial) {
-                    a[0] &= vmask[0];
-                    a[1] &= vmask[1];
-                    a[2] &= vmask[2];
-                    a[3] &= vmask[3];
                 }
                 o[dt] = mfma_k32<QDT>(a, ph, o[dt]);
                 o[dt] = mfma_k32<QDT>(a, pl, o[dt]);
@@ -566,11 +585,6 @@ phase1_kernel(const Phase1Params P) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) a[e] = as_f32(vr[i].w[e]);
                 }
-                if (vpartial) {
-                    const int t0 = start + unit_of(u) * UNIT + 8 * grp;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) a[e] = (t0 + e < L) ? a[e] : 0.0f;
-                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[dt] = mfma_k4(a[e], pr[e], o[dt]);
             }
@@ -579,7 +593,7 @@ phase1_kernel(const Phase1Params P) {
     }
     lsum = wave_sum_groups(lsum);
     if constexpr (S::kF32) lsum_r = lsum;
-    else lsum_r = wave_sum_groups(lsum_r);
+    else lsum_r = osum[0];
 
     // ---- merge the wavefronts through LDS ---------------------------------------
     constexpr int RS = S::kD16 + 4;   // row stride (floats) of s_o

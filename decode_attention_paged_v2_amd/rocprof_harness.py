@@ -1,7 +1,7 @@
 """rocprofv3 harness: per-kernel durations and HBM traffic of the decode path.
 
     python -m decode_attention_paged_v2_amd.rocprof_harness --config long_gqa \
-        --out gpurun_out/prof [--pmc]
+        --out gpurun_out/prof [--pmc] [--sq]
 
 Runs `bench.py` (a few steps, no CPU baseline) under
 
@@ -10,7 +10,9 @@ Runs `bench.py` (a few steps, no CPU baseline) under
 * with `--pmc`, two counter passes (`FETCH_SIZE`, then `WRITE_SIZE`, KiB per
   dispatch) over the same command and over `bench.py --mode copy` (a plain
   1 GiB copy).  Each counter is scaled by the ratio of the copy's known bytes
-  to what the counter reports for it, giving HBM bytes per phase-1 launch.
+  to what the counter reports for it, giving HBM bytes per phase-1 launch;
+* with `--sq`, two passes of SQ instruction counters over phase 1, reported
+  per (work item, wavefront).
 
 Writes `<out>/<kernel>_<config>.md` (a short summary with the commands) and
 `<out>/<kernel>_<config>.json` (the numbers, plus a hash of the kernel sources
@@ -130,13 +132,51 @@ def pmc(config: str, out: str) -> dict:
     return res
 
 
+SQ_PASSES = [
+    ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS", "SQ_INSTS_SALU"],
+    ["SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_SMEM", "SQ_INSTS_BRANCH"],
+]
+
+
+def sq(config: str, out: str) -> dict:
+    """Instruction mix of phase 1: kernel-wide SQ instruction counts, two passes."""
+    vals = {}
+    for i, counters in enumerate(SQ_PASSES):
+        d = os.path.join(out, f"sq{i}_{config}")
+        shutil.rmtree(d, ignore_errors=True)
+        bench = [sys.executable, BENCH, "--config", config, "--steps", "3", "--warmup", "1",
+                 "--no-cpu-baseline", "--flush-steps", "0"]
+        cmd = ["rocprofv3", "--pmc", *counters, "-d", d, "-o", "run", "--output-format", "csv", "--"] + bench
+        _run(cmd, os.path.join(out, f"sq{i}_{config}.log"), 120)
+        per = {}
+        for r in _csv(os.path.join(d, "**", "run_counter_collection.csv")):
+            if _kind(r["Kernel_Name"]) != "phase1":
+                continue
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for k, v in per.items():
+            vals[k] = sum(v) / len(v)
+        vals.setdefault("commands", []).append(" ".join(cmd[:-len(bench)]) + " -- python bench.py " +
+                                               " ".join(bench[2:]))
+    return vals
+
+
+def phase1_waves(config: str) -> int:
+    """Wavefronts per phase-1 workgroup, from the library's host-side launch plan."""
+    from . import _binding as B, workloads
+    sp = workloads.SPECS[config]
+    code = {"f32": B.F32, "f16": B.F16, "bf16": B.BF16, "fp8_e4m3": B.FP8_E4M3}
+    pl = B.plan(1, sp.num_heads, sp.num_kv_heads, sp.head_size, sp.block_size, 1,
+                code[sp.q_dtype], code[sp.kv_dtype])
+    return pl["phase1_threads"] // 64
+
+
 def algorithmic_bytes(config: str) -> dict:
     """Phase-1 / phase-2 algorithmic bytes of the workload (host-side, no GPU)."""
     from . import accounting, workloads
     return accounting.spec_bytes(workloads.SPECS[config])
 
 
-def write_summary(config: str, out: str, trace: dict, counters: dict | None) -> str:
+def write_summary(config: str, out: str, trace: dict, counters: dict | None, sqv: dict | None = None) -> str:
     alg = algorithmic_bytes(config)
     p1 = trace["phase1"]
     name = "phase1_" + config
@@ -144,7 +184,7 @@ def write_summary(config: str, out: str, trace: dict, counters: dict | None) -> 
              f"Kernel sources hash: `{source_hash()}`", "",
              "Kernel trace command (from the repository root):", "",
              "    python -m decode_attention_paged_v2_amd.rocprof_harness --config "
-             f"{config} --out gpurun_out/prof{' --pmc' if counters else ''}", "",
+             f"{config} --out gpurun_out/prof{' --pmc' if counters else ''}{' --sq' if sqv else ''}", "",
              "which runs:", "", "    " + trace["command"], "",
              "| kernel | calls | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|"]
     for k in ("phase1", "phase2"):
@@ -176,6 +216,20 @@ def write_summary(config: str, out: str, trace: dict, counters: dict | None) -> 
                   f"| algorithmic reads / writes | {alg['phase1_read']:,} / {alg['phase1_write']:,} |",
                   f"| measured / algorithmic | reads {f1 / alg['phase1_read']:.4f}, "
                   f"writes {w1 / alg['phase1_write']:.4f} |"]
+    if sqv:
+        data["sq"] = sqv
+        # every wavefront of a work item runs the same unrolled unit loop, so
+        # counts per (item, wavefront) are the per-item instruction budget
+        waves = phase1_waves(config)
+        per = alg["phase1_items"] * waves
+        lines += ["", f"Instruction mix of phase 1 (rocprofv3 `--pmc` SQ counters, kernel-wide totals "
+                  f"divided by {alg['phase1_items']:,} work items x {waves} wavefronts):", ""]
+        lines += ["    " + c for c in sqv["commands"]]
+        lines += ["", "| counter | per (item, wavefront) |", "|---|---|"]
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA",
+                  "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_SMEM", "SQ_INSTS_BRANCH"):
+            if k in sqv:
+                lines.append(f"| {k} | {sqv[k] / per:.1f} |")
     with open(os.path.join(out, name + ".md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     with open(os.path.join(out, name + ".json"), "w") as fh:
@@ -187,14 +241,16 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="long_gqa")
     ap.add_argument("--out", default="gpurun_out/prof")
-    ap.add_argument("--pmc", action="store_true")
+    ap.add_argument("--pmc", action="store_true", help="HBM FETCH_SIZE / WRITE_SIZE passes")
+    ap.add_argument("--sq", action="store_true", help="instruction-mix / utilisation passes")
     ap.add_argument("--steps", type=int, default=10)
     a = ap.parse_args()
     out = os.path.abspath(a.out)
     os.makedirs(out, exist_ok=True)
     trace = kernel_trace(a.config, out, a.steps)
     counters = pmc(a.config, out) if a.pmc else None
-    path = write_summary(a.config, out, trace, counters)
+    sqv = sq(a.config, out) if a.sq else None
+    path = write_summary(a.config, out, trace, counters, sqv)
     print(open(path).read(), flush=True)
 
 

@@ -1,0 +1,42 @@
+"""Byte accounting used by the benchmark, checked against the footprint
+numbers the pages print (tests/golden/page_numbers.json)."""
+import json
+import os
+
+import pytest
+
+from decode_attention_paged_v2_amd import accounting, workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")
+
+
+def _entries():
+    with open(GOLDEN) as fh:
+        return json.load(fh)["entries"]
+
+
+def test_expanded_kv_footprint_and_gqa_saving():
+    e, s, _ = _entries()
+    L, H, KVH, D, b = e["seq_len"], e["num_heads"], e["num_kv_heads"], e["head_size"], e["elem_bytes"]
+    expanded_k = accounting.kv_bytes([L], H, D, b) // 2          # K alone, one head per query head
+    grouped_k = accounting.kv_bytes([L], KVH, D, b) // 2
+    assert expanded_k == pytest.approx(e["value_bytes_approx"], rel=e["rel_tol"])
+    assert expanded_k - grouped_k == pytest.approx(s["saving_bytes_approx"], rel=s["rel_tol"])
+    assert expanded_k // grouped_k == H // KVH
+
+
+def test_partition_count():
+    p = _entries()[2]
+    assert (100000 + accounting.PARTITION_SIZE - 1) // accounting.PARTITION_SIZE == p["value"]
+    assert p["value"] == p["page_value"] + 1
+
+
+def test_long_context_workload_bytes():
+    b = accounting.spec_bytes(W.SPECS["long_gqa"])
+    # 4 sequences x 100000 tokens x 4 kv heads x (K + V) x 256 x 2 bytes
+    assert b["kv"] == 4 * 100000 * 4 * 2 * 256 * 2 == 1_638_400_000
+    # plus query, 6250 block ids per sequence, seq_lens
+    assert b["phase1_read"] == b["kv"] + 4 * 24 * 256 * 2 + 4 * 4 * 6250 + 4 * 4
+    # tmp rows of 196 partitions per (seq, head) and two float32 statistics per slot
+    assert b["phase1_write"] == 4 * 24 * 196 * 256 * 2 + 8 * 4 * 24 * 196
+    assert b["phase1"] == b["phase1_read"] + b["phase1_write"]
