@@ -155,8 +155,9 @@ def sq(config: str, out: str) -> dict:
             per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
         for k, v in per.items():
             vals[k] = sum(v) / len(v)
-        vals.setdefault("commands", []).append(" ".join(cmd[:-len(bench)]) + " -- python bench.py " +
-                                               " ".join(bench[2:]))
+        vals.setdefault("commands", []).append(
+            f"rocprofv3 --pmc {' '.join(counters)} -d gpurun_out/prof/sq{i}_{config} -o run "
+            f"--output-format csv -- python3 bench.py {' '.join(bench[2:])}")
     return vals
 
 

@@ -327,6 +327,29 @@ def test_spare_partition_slots_and_inflated_max_seq_len():
     compare(wl, g, run_oracle(wl))
 
 
+def test_dense_schedule_for_large_batches_with_spare_slots():
+    """Batches of more than 8192 sequences run on the dense grid (one
+    workgroup per partition slot); an inflated max_seq_len leaves most slots
+    past their sequence's end."""
+    n = 8193
+    spec = W.Spec("many", 4, 2, 64, 16, "f16", "f16",
+                  lambda g: [1300, 600, 0] + torch.randint(0, 40, (n - 3,), generator=g).tolist(),
+                  alibi=True, seed=21)
+    wl = W.generate(spec, poison=True)
+    plan = pav2.plan(n, 4, 2, 64, 16, 6, pav2.F16, pav2.F16)
+    assert plan["phase1_compact"] == 0
+    wl.max_seq_len = 3000
+    wl.max_num_partitions = 6
+    pad = torch.full((n, 188), -1, dtype=torch.int32)
+    pad[:, :wl.block_tables.shape[1]] = wl.block_tables
+    wl.block_tables = pad
+    g = run_gpu(wl.to(DEV))
+    rng = np.random.default_rng(5)
+    pairs = sorted({(0, h) for h in range(4)} | {(1, 3), (2, 0), (n - 1, 2)} |
+                   {(int(a), int(b)) for a, b in zip(rng.integers(0, n, 300), rng.integers(0, 4, 300))})
+    compare(wl, g, run_oracle(wl, pairs=pairs), pairs=pairs)
+
+
 def test_single_sequence_dense_schedule_with_spare_slots():
     """One sequence runs on the dense grid (one workgroup per partition slot);
     an inflated max_seq_len makes most slots start past the sequence end."""
