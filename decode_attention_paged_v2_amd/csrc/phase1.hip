@@ -150,7 +150,8 @@ __device__ __forceinline__ T load_stream(const uint8_t *p) {
         return *reinterpret_cast<const T *>(p);
 }
 
-template <int QDT, int KVDT, int D, int WAVES, bool COMPACT>
+// BS: the block size when fixed at compile time (16 or 32), 0 for any.
+template <int QDT, int KVDT, int D, int WAVES, bool COMPACT, int BS>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(kPhase1Occupancy)))
 phase1_kernel(const Phase1Params P) {
     using S = Shape<QDT, KVDT, D>;
@@ -168,6 +169,9 @@ phase1_kernel(const Phase1Params P) {
     const int HG = P.head_groups;
     const int KVH = P.num_kv_heads;
     const int heads_alloc = min(P.gqa, kMaxHeadsPerGroup);
+    constexpr int kBsLog2 = BS == 16 ? 4 : (BS == 32 ? 5 : -1);
+    const int bs_log2 = kBsLog2 >= 0 ? kBsLog2 : P.bs_log2;
+    const int bs_mask = (1 << bs_log2) - 1;
     // LDS: per-wave partial outputs, per-wave max/sums, the partition's
     // block-table slice, then (compact schedule) the partition-count prefix.
     float *s_o = reinterpret_cast<float *>(smem);
@@ -175,7 +179,7 @@ phase1_kernel(const Phase1Params P) {
     float *s_l = s_m + WAVES * kMaxHeadsPerGroup;
     float *s_lr = s_l + WAVES * kMaxHeadsPerGroup;
     int *s_bt = reinterpret_cast<int *>(s_lr + WAVES * kMaxHeadsPerGroup);
-    int *s_pref = s_bt + (kPartition >> P.bs_log2);     // [num_seqs + 1]
+    int *s_pref = s_bt + (kPartition >> bs_log2);       // [num_seqs + 1]
     int *s_wsum = s_pref + P.num_seqs + 1;              // [WAVES]
 
     // Work items.  Dense schedule: one (partition, seq, kv head, head group)
@@ -281,8 +285,6 @@ phase1_kernel(const Phase1Params P) {
     const int n_tok = min(kPartition, L - start);
     const int last = start + n_tok - 1;   // ALiBi reference position: the partition's last token
 
-    const int bs_log2 = P.bs_log2;
-    const int bs_mask = (1 << bs_log2) - 1;
     {
         const int n_all = kPartition >> bs_log2;
         const int n_used = (n_tok + bs_mask) >> bs_log2;
@@ -346,8 +348,17 @@ phase1_kernel(const Phase1Params P) {
     auto load_k = [&](u32x4 (&dst)[NKL], int u, int half) {
         const int t = clamp_unit(unit_of(u));
         const int o = t * UNIT + 16 * half + col;            // token offset in partition
-        const int64_t b = s_bt[o >> bs_log2];
-        const uint8_t *base = kc + b * blk_stride + (o & bs_mask) * 16 + (grp << (bs_log2 + 4));
+        const uint8_t *base;
+        if constexpr (BS >= 16) {
+            // the tile's 16 tokens share one block: a wave-uniform block base
+            // plus a per-lane offset that does not change between tiles
+            const int64_t b = __builtin_amdgcn_readfirstlane(s_bt[(t * UNIT + 16 * half) >> bs_log2]);
+            const uint32_t lane_off = (uint32_t)((o & bs_mask) * 16 + (grp << (bs_log2 + 4)));
+            base = kc + b * blk_stride + lane_off;
+        } else {
+            const int64_t b = s_bt[o >> bs_log2];
+            base = kc + b * blk_stride + (o & bs_mask) * 16 + (grp << (bs_log2 + 4));
+        }
 #pragma unroll
         for (int w = 0; w < NKL; ++w) {
             u32x4 v = {0, 0, 0, 0};
@@ -359,8 +370,16 @@ phase1_kernel(const Phase1Params P) {
     auto load_v = [&](Words<VW> (&dst)[DPG], int u, int part) {
         const int t = clamp_unit(unit_of(u));
         const int o = t * UNIT + 8 * grp;                    // first of the lane's 8 tokens
-        const int64_t b = s_bt[o >> bs_log2];
-        const uint8_t *base = vc + b * blk_stride + (o & bs_mask) * KVB + (col << bs_log2) * KVB;
+        const uint8_t *base;
+        if constexpr (BS >= 32) {
+            // the unit's 32 tokens share one block
+            const int64_t b = __builtin_amdgcn_readfirstlane(s_bt[(t * UNIT) >> bs_log2]);
+            const uint32_t lane_off = (uint32_t)(((o & bs_mask) + (col << bs_log2)) * KVB);
+            base = vc + b * blk_stride + lane_off;
+        } else {
+            const int64_t b = s_bt[o >> bs_log2];
+            base = vc + b * blk_stride + (o & bs_mask) * KVB + (col << bs_log2) * KVB;
+        }
 #pragma unroll
         for (int i = 0; i < DPG; ++i) {
             const int dt = part * DPG + i;
@@ -687,10 +706,10 @@ int device_cu_count() {
     return cache[dev];
 }
 
-template <int QDT, int KVDT, int D, bool COMPACT>
+template <int QDT, int KVDT, int D, bool COMPACT, int BS>
 hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
     constexpr int WAVES = kPhase1Waves;
-    const void *fn = reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, COMPACT>);
+    const void *fn = reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, COMPACT, BS>);
     if (lds > 65536) hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     int grid = (p.num_work + 7) / 8 * 8;
     if (COMPACT) {
@@ -703,15 +722,28 @@ hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
         const int cap = kPhase1CompactRounds * device_cu_count() * per_cu;
         grid = grid < cap ? grid : cap;
     }
-    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, COMPACT>), dim3(grid), dim3(WAVES * 64), lds,
+    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, COMPACT, BS>), dim3(grid), dim3(WAVES * 64), lds,
                        stream, p);
     return hipGetLastError();
 }
 
+// Block sizes 16 and 32 (16-bit queries) get kernels with the block size
+// fixed at compile time (load offsets become immediates; the block of a
+// 16-token K tile, and at 32 of a whole unit, is wave-uniform); every other
+// case runs the generic kernel.
+template <int QDT, int KVDT, int D, bool COMPACT>
+hipError_t launch_bs(const Phase1Params &p, int lds, hipStream_t stream) {
+    if constexpr (QDT != F32) {
+        if (p.bs_log2 == 4) return launch_sched<QDT, KVDT, D, COMPACT, 16>(p, lds, stream);
+        if (p.bs_log2 == 5) return launch_sched<QDT, KVDT, D, COMPACT, 32>(p, lds, stream);
+    }
+    return launch_sched<QDT, KVDT, D, COMPACT, 0>(p, lds, stream);
+}
+
 template <int QDT, int KVDT, int D>
 hipError_t launch_one(const Phase1Params &p, int lds, hipStream_t stream) {
-    return p.compact ? launch_sched<QDT, KVDT, D, true>(p, lds, stream)
-                     : launch_sched<QDT, KVDT, D, false>(p, lds, stream);
+    return p.compact ? launch_bs<QDT, KVDT, D, true>(p, lds, stream)
+                     : launch_bs<QDT, KVDT, D, false>(p, lds, stream);
 }
 
 template <int QDT, int KVDT>

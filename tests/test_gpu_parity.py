@@ -350,6 +350,37 @@ def test_dense_schedule_for_large_batches_with_spare_slots():
     compare(wl, g, run_oracle(wl, pairs=pairs), pairs=pairs)
 
 
+# Batches with many partition slots (an inflated max_seq_len: most slots lie
+# past their sequence's end) and ragged lengths, across dtypes and head
+# sizes, at sizes the oracle covers completely.
+MANY_SLOT_CASES = [
+    ("f16", "f16", 32, 8, 80, 16, True),
+    ("bf16", "fp8_e4m3", 64, 8, 128, 32, False),
+    ("bf16", "bf16", 24, 4, 256, 16, False),
+    ("f32", "f32", 8, 8, 64, 16, True),
+    ("f16", "f16", 16, 2, 120, 8, False),
+]
+
+
+@pytest.mark.parametrize("qd,kvd,H,KVH,d,bs,alibi", MANY_SLOT_CASES)
+def test_many_partition_slots(qd, kvd, H, KVH, d, bs, alibi):
+    n = 64
+    maxP = -(-12288 // (n * KVH * max(1, -(-(H // KVH) // 16))))
+    lens = lambda g: [0, 1, 511, 512, 513, 2047, 2600] + torch.randint(1, 2600, (n - 7,), generator=g).tolist()
+    spec = W.Spec("slots", H, KVH, d, bs, qd, kvd, lens, alibi=alibi, seed=31,
+                  k_scale=0.05 if kvd == "fp8_e4m3" else 1.0, v_scale=0.04 if kvd == "fp8_e4m3" else 1.0)
+    wl = W.generate(spec, poison=True)
+    wl.max_seq_len = maxP * 512
+    wl.max_num_partitions = maxP
+    mbps = -(-wl.max_seq_len // bs)
+    pad = torch.full((n, mbps), -1, dtype=torch.int32)
+    pad[:, :wl.block_tables.shape[1]] = wl.block_tables
+    wl.block_tables = pad
+    g = run_gpu(wl.to(DEV))
+    worst = compare(wl, g, run_oracle(wl))
+    say(f"  worst {worst}")
+
+
 def test_single_sequence_dense_schedule_with_spare_slots():
     """One sequence runs on the dense grid (one workgroup per partition slot);
     an inflated max_seq_len makes most slots start past the sequence end."""
