@@ -62,6 +62,8 @@ def load():
         L.pav2_plan.restype = I
         L.pav2_decode_kv.argtypes = [P, P, ctypes.c_int64, I, I, P]
         L.pav2_decode_kv.restype = I
+        L.pav2_check_inputs.argtypes = [P, P, I, I, I, I, P, P]
+        L.pav2_check_inputs.restype = I
         L.pav2_max_num_partitions.argtypes = [I]
         L.pav2_max_num_partitions.restype = I
         L.pav2_last_error.argtypes = []
@@ -209,6 +211,30 @@ def decode_kv(src, compute_dtype=None, stream=None):
                                _stream(src, stream))
     _check(rc)
     return dst.view(src.shape)
+
+
+def check_inputs(block_tables, seq_lens, block_size, num_blocks, stream=None) -> dict:
+    """Run the device-side validator of block tables and sequence lengths and
+    return its report (this synchronises with the stream)."""
+    import torch
+    S, mbps = (int(v) for v in block_tables.shape)
+    if tuple(seq_lens.shape) != (S,):
+        raise ValueError("seq_lens must have shape [num_seqs]")
+    _i32(block_tables, "block_tables")
+    _i32(seq_lens, "seq_lens")
+    report = torch.empty(4, dtype=torch.int64, device=block_tables.device)
+    st = _stream(block_tables, stream)
+    rc = load().pav2_check_inputs(_dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S, mbps,
+                                  int(block_size), int(num_blocks), _dev(report, "report"), st)
+    _check(rc)
+    if stream is None:
+        torch.cuda.current_stream(block_tables.device).synchronize()
+    elif hasattr(stream, "synchronize"):
+        stream.synchronize()
+    else:
+        torch.cuda.synchronize(block_tables.device)
+    r = [int(v) for v in report.cpu()]
+    return {"bad_sequences": r[0], "first_sequence": r[1], "first_column": r[2], "value": r[3]}
 
 
 def decode(query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, scale,

@@ -302,6 +302,22 @@ int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype
                          "decode_kv");
 }
 
+int pav2_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                      int max_blocks_per_seq, int block_size, int num_blocks, int64_t *report,
+                      pav2_stream_t stream) {
+    g_err[0] = 0;
+    if (!report) return fail(PAV2_ERR_INVALID_ARGUMENT, "report is NULL");
+    if (num_seqs < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", num_seqs);
+    if (max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "max_blocks_per_seq, block_size and num_blocks must be > 0");
+    if (num_seqs > 0 && (!block_tables || !seq_lens))
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    return launch_status(pav2::launch_check_inputs(block_tables, seq_lens, num_seqs, max_blocks_per_seq,
+                                                   block_size, num_blocks, reinterpret_cast<long long *>(report),
+                                                   static_cast<hipStream_t>(stream)),
+                         "check_inputs");
+}
+
 int pav2_max_num_partitions(int max_seq_len) {
     if (max_seq_len <= 0) return 0;
     return (int)(((int64_t)max_seq_len + PAV2_PARTITION_SIZE - 1) / PAV2_PARTITION_SIZE);

@@ -168,6 +168,22 @@ int pav2_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size,
 int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype,
                    pav2_dtype_t compute_dtype, pav2_stream_t stream);
 
+/*
+ * Debug validator for the device data the decode entry points take on trust:
+ * every seq_lens[s] in [0, max_blocks_per_seq * block_size], and every
+ * block_tables[s][j] with j < ceil(seq_lens[s] / block_size) in
+ * [0, num_blocks).  Writes, asynchronously on `stream`, into `report`
+ * (4 int64 in device memory, owned by the caller; read it after the stream
+ * has synchronised): report[0] = number of offending sequences,
+ * report[1] = the first one (-1 if none), report[2] = its first offending
+ * block-table column (-1 when its length is out of range), report[3] = the
+ * offending value.  Allocates nothing; returns PAV2_ERR_INVALID_ARGUMENT for
+ * null pointers or non-positive sizes, PAV2_ERR_LAUNCH if a launch fails.
+ */
+int pav2_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                      int max_blocks_per_seq, int block_size, int num_blocks, int64_t *report,
+                      pav2_stream_t stream);
+
 /* ceil(max_seq_len / 512): the partition count a sequence of that length needs. */
 int pav2_max_num_partitions(int max_seq_len);
 

@@ -100,6 +100,17 @@ def test_phase2_validation():
     assert lib.pav2_phase2(None, None, None, None, None, 0, 24, 256, 196, B.BF16, None) == 0
 
 
+def test_check_inputs_validation():
+    lib = pav2.load()
+    v = ctypes.c_void_p(16)
+    assert lib.pav2_check_inputs(v, v, 4, 10, 16, 100, None, None) == -1
+    assert "report" in pav2.last_error()
+    assert lib.pav2_check_inputs(v, v, -1, 10, 16, 100, v, None) == -1
+    assert lib.pav2_check_inputs(v, v, 4, 0, 16, 100, v, None) == -1
+    assert lib.pav2_check_inputs(v, v, 4, 10, 16, 0, v, None) == -1
+    assert lib.pav2_check_inputs(None, v, 4, 10, 16, 100, v, None) == -1
+
+
 def test_decode_kv_validation():
     lib = pav2.load()
     v = ctypes.c_void_p(16)
