@@ -7,7 +7,9 @@ the C ABI on the current stream, on synthetic inputs already resident in HBM.
 
 Default workload: 4 sequences x 100000 tokens, 24 query heads over 4 kv heads
 (GQA 6), head size 256, bf16, block size 16 -- the long-context GQA decode the
-metric names.  `--config` selects one of the other workloads.
+metric names.  `--config` selects one of the other workloads.  `--entry v1`
+times the single-pass entry point instead (one launch per step), `--entry
+auto` whichever of the two the library's planner picks for the workload.
 
 Prints ONE JSON line.  `value` is KV bytes read per second (decimal GB/s);
 `roofline` reports phase 1's algorithmic bytes per launch over its mean
@@ -89,12 +91,13 @@ def cpu_baseline(wl, out_gpu, target_core_seconds=15.0, max_threads=16):
     }
 
 
-def measured_traffic(config):
+def measured_traffic(config, entry="v2"):
     """HBM bytes per phase-1 launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain
     copy's reading) from the committed counter summary, or None when there is
     none or it was taken on different kernel sources."""
     from decode_attention_paged_v2_amd import rocprof_harness
-    path = os.path.join(ROOT, "profiles", f"phase1_{config}.json")
+    name = f"phase1_{config}.json" if entry == "v2" else f"v1_{config}.json"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -128,6 +131,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="long_gqa", choices=list(W.SPECS))
+    ap.add_argument("--entry", default="v2", choices=["v2", "v1", "auto"],
+                    help="v2: both phases (the default); v1: the single-pass entry point; "
+                         "auto: the planner's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="extra per-step timings with a 1 GiB cache flush before each step")
@@ -164,14 +170,21 @@ def main():
          wl.seq_lens, wl.block_size, wl.max_seq_len)
     kw = dict(alibi_slopes=wl.alibi_slopes, k_scale=wl.k_scale, v_scale=wl.v_scale)
     stream = torch.cuda.current_stream(dev)
+    plan = pav2.plan(S, H, wl.num_kv_heads, D, wl.block_size, P, pav2._binding._dtype_code(wl.query),
+                     pav2._binding._dtype_code(wl.key_cache))
+    entry = args.entry if args.entry != "auto" else ("v1" if plan["use_v1"] else "v2")
 
     def step(ev_a=None, ev_b=None):
         if ev_a is not None:
             ev_a.record(stream)
-        pav2.phase1(es, ml, tmp, *a, **kw)
+        if entry == "v1":
+            pav2.paged_attention_v1(out, *a, **kw)
+        else:
+            pav2.phase1(es, ml, tmp, *a, **kw)
         if ev_b is not None:
             ev_b.record(stream)
-        pav2.phase2(out, es, ml, tmp, wl.seq_lens)
+        if entry == "v2":
+            pav2.phase2(out, es, ml, tmp, wl.seq_lens)
 
     for _ in range(args.warmup):
         step()
@@ -203,8 +216,8 @@ def main():
         del scratch
 
     kv = wl.kv_bytes()
-    b1 = accounting.workload_bytes(wl)["phase1"]
-    traffic = measured_traffic(args.config)
+    b1 = accounting.workload_bytes(wl)["phase1" if entry == "v2" else "v1"]
+    traffic = measured_traffic(args.config, entry)
     p1_mean = float(np.mean(p1_ms))
     achieved = b1 / (p1_mean * 1e-3) / 1e9
     value = kv / (ms_per_step * 1e-3) / 1e9
@@ -228,6 +241,7 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "tokens_heads_per_s": round(wl.tokens_heads() / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv,
+        "entry": entry,
         "phase1_ms_mean": round(p1_mean, 5),
         "phase1_ms_min": round(float(np.min(p1_ms)), 5),
         "phase2_plus_gap_ms": round(ms_per_step - p1_mean, 5),
@@ -235,7 +249,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "phase1_kernel", "algorithmic_bytes_per_launch": b1},
+                     "kernel": "phase1_kernel" + (" (single pass)" if entry == "v1" else ""),
+                     "algorithmic_bytes_per_launch": b1},
         "generate_s": round(gen_s, 2),
         "library": pav2.lib_path(),
     }

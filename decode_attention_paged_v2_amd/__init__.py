@@ -6,6 +6,7 @@ whose functions carry the same names as the C entry points.  The library is
 loaded on first use; there is no CPU fallback.
 """
 from ._binding import (  # noqa: F401
-    BF16, F16, F32, FP8_E4M3, PARTITION_SIZE, Pav2Error, check_inputs, decode, decode_kv, last_error,
-    lib_path, load, max_num_partitions, paged_attention_v2, phase1, phase2, plan, version,
+    BF16, F16, F32, FP8_E4M3, PARTITION_SIZE, Pav2Error, check_inputs, decode, decode_kv, forward_decode,
+    last_error, lib_path, load, max_num_partitions, paged_attention_v1, paged_attention_v2, phase1, phase2,
+    plan, version,
 )

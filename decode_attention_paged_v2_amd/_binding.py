@@ -29,7 +29,7 @@ class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "phase1_workgroups", "phase1_threads", "phase1_lds_bytes", "head_groups",
         "waves_per_partition", "phase2_workgroups", "phase2_threads", "phase2_lds_bytes",
-        "phase1_compact")]
+        "phase1_compact", "use_v1", "v1_workgroups", "v1_lds_bytes")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -54,6 +54,8 @@ def load():
         attn = [P, P, P, P, P, P, P, I, F, P, P, I, I, P, I, F, F, I, I, I, I, I, I, I, P]
         L.pav2_paged_attention_v2.argtypes = attn
         L.pav2_paged_attention_v2.restype = I
+        L.pav2_paged_attention_v1.argtypes = [P, P, P, P, I, F, P, P, I, I, P, I, F, F, I, I, I, I, I, I, P]
+        L.pav2_paged_attention_v1.restype = I
         L.pav2_phase1.argtypes = attn[1:]
         L.pav2_phase1.restype = I
         L.pav2_phase2.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
@@ -164,6 +166,25 @@ def paged_attention_v2(output, exp_sums, max_logits, tmp_output, query, key_cach
     _check(rc)
 
 
+def paged_attention_v1(output, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+                       seq_lens, block_size, max_seq_len, alibi_slopes=None, kv_cache_dtype="auto",
+                       k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """The pages' V1 op (single pass): fills output in place."""
+    L = load()
+    S, H, D, kvdt = _common(query, key_cache, value_cache, num_kv_heads, block_tables, seq_lens,
+                            block_size, kv_cache_dtype, alibi_slopes)
+    if tuple(output.shape) != (S, H, D) or output.dtype != query.dtype:
+        raise ValueError("output must match query in shape and dtype")
+    rc = L.pav2_paged_attention_v1(
+        _dev(output, "output"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), int(num_kv_heads), float(scale),
+        _i32(block_tables, "block_tables"), _i32(seq_lens, "seq_lens"), int(block_size),
+        int(max_seq_len), _dev(alibi_slopes, "alibi_slopes"), kvdt, float(k_scale), float(v_scale),
+        S, H, D, int(key_cache.shape[0]), int(block_tables.shape[1]), _dtype_code(query),
+        _stream(query, stream))
+    _check(rc)
+
+
 def phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, num_kv_heads, scale,
            block_tables, seq_lens, block_size, max_seq_len, alibi_slopes=None,
            kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0, stream=None) -> None:
@@ -256,3 +277,26 @@ def decode(query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, 
                        num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                        alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
     return output, exp_sums, max_logits, tmp_output
+
+
+def forward_decode(query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, scale,
+                   block_size, max_seq_len, alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0,
+                   v_scale=1.0, stream=None):
+    """Decode attention with the V1 / V2 choice of page "paged_attn.py"
+    (forward_decode), taken by the library's planner (``plan()["use_v1"]``).
+
+    Returns the output tensor.
+    """
+    import torch
+    S, H, D = (int(v) for v in query.shape)
+    P = max(1, max_num_partitions(max_seq_len))
+    kvdt = _dtype_code(key_cache, kv_cache_dtype)
+    pl = plan(S, H, num_kv_heads, D, block_size, P, _dtype_code(query), kvdt)
+    if pl["use_v1"]:
+        output = torch.empty_like(query)
+        paged_attention_v1(output, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+                           seq_lens, block_size, max_seq_len, alibi_slopes, kv_cache_dtype, k_scale,
+                           v_scale, stream)
+        return output
+    return decode(query, key_cache, value_cache, block_tables, seq_lens, num_kv_heads, scale,
+                  block_size, max_seq_len, alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)[0]

@@ -5,7 +5,8 @@ bytes per (token, kv head), shared by the kv head's query heads -- plus the
 query and the block-table entries the sequences use, and writes one
 tmp_output row and two float32 statistics per (seq, head, used partition)
 plus the statistics of the unused slots.  Phase 2 reads the used partitions'
-rows and statistics and writes the output.
+rows and statistics and writes the output.  The single-pass (V1) kernel reads
+what phase 1 reads and writes only the output.
 """
 from __future__ import annotations
 
@@ -40,6 +41,11 @@ def phase2_bytes(lens, num_heads, head_size, q_elem_bytes) -> int:
     return used_parts * num_heads * (head_size * q_elem_bytes + 8) + S * num_heads * head_size * q_elem_bytes + 4 * S
 
 
+def v1_bytes(lens, num_heads, num_kv_heads, head_size, block_size, q_elem_bytes, kv_elem_bytes) -> int:
+    return (phase1_read_bytes(lens, num_heads, num_kv_heads, head_size, block_size, q_elem_bytes, kv_elem_bytes)
+            + len(lens) * num_heads * head_size * q_elem_bytes)
+
+
 def workload_bytes(wl) -> dict:
     """The counts for a generated workload (decode_attention_paged_v2_amd.workloads.Workload)."""
     qb = wl.query.element_size()
@@ -50,6 +56,7 @@ def workload_bytes(wl) -> dict:
         "phase1": phase1_bytes(lens, wl.num_heads, wl.num_kv_heads, wl.head_size, wl.block_size, qb, kvb,
                                wl.max_num_partitions),
         "phase2": phase2_bytes(lens, wl.num_heads, wl.head_size, qb),
+        "v1": v1_bytes(lens, wl.num_heads, wl.num_kv_heads, wl.head_size, wl.block_size, qb, kvb),
     }
 
 
@@ -75,4 +82,5 @@ def spec_bytes(spec) -> dict:
                                          spec.block_size, qb, kvb),
         "phase1_write": phase1_write_bytes(lens, spec.num_heads, spec.head_size, qb, maxP),
         "phase2": phase2_bytes(lens, spec.num_heads, spec.head_size, qb),
+        "v1": v1_bytes(lens, spec.num_heads, spec.num_kv_heads, spec.head_size, spec.block_size, qb, kvb),
     }

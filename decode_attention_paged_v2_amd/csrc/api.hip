@@ -128,6 +128,9 @@ void make_plan(const Shape &s, pav2_plan_t *pl) {
         pl->phase2_threads = 64 * (wpp > 4 ? wpp : 4);
     }
     pl->phase2_lds_bytes = pav2::phase2_lds_bytes(s.max_num_partitions, s.head_size, s.qdt);
+    pl->use_v1 = pav2::prefer_single_pass((int64_t)s.num_seqs * s.num_kv_heads * hg, s.max_num_partitions) ? 1 : 0;
+    pl->v1_workgroups = (int)((int64_t)s.num_seqs * s.num_kv_heads * hg);
+    pl->v1_lds_bytes = pav2::phase1_lds_bytes(gqa, s.head_size, pav2::kPhase1Waves, bs_log2, s.num_seqs, false);
 }
 
 int launch_status(hipError_t e, const char *what) {
@@ -162,7 +165,7 @@ int run_phase1(float *exp_sums, float *max_logits, void *tmp_output, const void 
     p.max_blocks_per_seq = sh.max_blocks_per_seq;
     p.max_num_partitions = sh.max_num_partitions;
     p.num_work = sh.num_seqs * sh.num_kv_heads * pl.head_groups * sh.max_num_partitions;
-    p.compact = pl.phase1_compact;
+    p.sched = pl.phase1_compact;
     p.head_stride = (int64_t)sh.head_size * sh.block_size * elem_bytes(sh.kvdt);
     p.blk_stride = p.head_stride * sh.num_kv_heads;
     p.scale_log2 = scale * k_scale * 1.4426950408889634f;
@@ -170,6 +173,42 @@ int run_phase1(float *exp_sums, float *max_logits, void *tmp_output, const void 
     return launch_status(pav2::launch_phase1(p, sh.qdt, sh.kvdt, sh.head_size, pl.waves_per_partition,
                                              pl.phase1_lds_bytes, stream),
                          "phase 1");
+}
+
+// Single pass: the phase-1 kernel walks all partitions of each (sequence, kv
+// head, head group) and writes the output itself.
+int run_v1(void *output, const void *query, const void *key_cache, const void *value_cache, float scale,
+           const int32_t *block_tables, const int32_t *seq_lens, const float *alibi_slopes, float k_scale,
+           float v_scale, const Shape &sh, hipStream_t stream) {
+    pav2_plan_t pl;
+    make_plan(sh, &pl);
+    pav2::Phase1Params p;
+    p.tmp_out = output;
+    p.exp_sums = nullptr;
+    p.max_logits = nullptr;
+    p.query = query;
+    p.key_cache = static_cast<const uint8_t *>(key_cache);
+    p.value_cache = static_cast<const uint8_t *>(value_cache);
+    p.block_tables = block_tables;
+    p.seq_lens = seq_lens;
+    p.alibi = alibi_slopes;
+    p.num_seqs = sh.num_seqs;
+    p.num_heads = sh.num_heads;
+    p.num_kv_heads = sh.num_kv_heads;
+    p.gqa = sh.num_heads / sh.num_kv_heads;
+    p.head_groups = pl.head_groups;
+    p.bs_log2 = ilog2_exact(sh.block_size);
+    p.max_blocks_per_seq = sh.max_blocks_per_seq;
+    p.max_num_partitions = sh.max_num_partitions;
+    p.num_work = pl.v1_workgroups;
+    p.sched = 2;
+    p.head_stride = (int64_t)sh.head_size * sh.block_size * elem_bytes(sh.kvdt);
+    p.blk_stride = p.head_stride * sh.num_kv_heads;
+    p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+    p.v_scale = v_scale;
+    return launch_status(pav2::launch_phase1(p, sh.qdt, sh.kvdt, sh.head_size, pl.waves_per_partition,
+                                             pl.v1_lds_bytes, stream),
+                         "single pass");
 }
 
 int run_phase2(void *output, const float *exp_sums, const float *max_logits, const void *tmp_output,
@@ -270,6 +309,28 @@ int pav2_paged_attention_v2(void *output, float *exp_sums, float *max_logits, vo
     if (rc) return rc;
     return run_phase2(output, exp_sums, max_logits, tmp_output, seq_lens, num_seqs, num_heads,
                       head_size, max_num_partitions, (int)query_dtype, st);
+}
+
+int pav2_paged_attention_v1(void *output, const void *query, const void *key_cache,
+                            const void *value_cache, int num_kv_heads, float scale,
+                            const int32_t *block_tables, const int32_t *seq_lens, int block_size,
+                            int max_seq_len, const float *alibi_slopes, pav2_dtype_t kv_cache_dtype,
+                            float k_scale, float v_scale, int num_seqs, int num_heads, int head_size,
+                            int num_blocks, int max_blocks_per_seq, pav2_dtype_t query_dtype,
+                            pav2_stream_t stream) {
+    g_err[0] = 0;
+    const int maxp = pav2_max_num_partitions(max_seq_len);
+    Shape sh{num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks,
+             max_blocks_per_seq, maxp > 0 ? maxp : 1, max_seq_len, (int)query_dtype, (int)kv_cache_dtype};
+    int rc = check_shape(sh);
+    if (rc) return rc;
+    if (num_seqs == 0) return PAV2_OK;
+    if (!output || !query || !key_cache || !value_cache || !block_tables || !seq_lens)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (!isfinite(scale) || !isfinite(k_scale) || !isfinite(v_scale))
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "scale, k_scale and v_scale must be finite");
+    return run_v1(output, query, key_cache, value_cache, scale, block_tables, seq_lens, alibi_slopes, k_scale,
+                  v_scale, sh, static_cast<hipStream_t>(stream));
 }
 
 int pav2_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,

@@ -33,7 +33,7 @@ __device__ __forceinline__ uint32_t as_u32(float x) { return __builtin_bit_cast(
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t x) { return __builtin_bit_cast(f16x2, x); }
 
 struct Phase1Params {
-    void *tmp_out;                 // [S, H, maxP, D] out dtype
+    void *tmp_out;                 // [S, H, maxP, D] out dtype; single pass: the output [S, H, D]
     float *exp_sums;               // [S, H, maxP]
     float *max_logits;             // [S, H, maxP]
     const void *query;             // [S, H, D]
@@ -48,8 +48,8 @@ struct Phase1Params {
     int bs_log2;                   // log2(block_size)
     int max_blocks_per_seq;
     int max_num_partitions;
-    int num_work;                  // S * KVH * head_groups * maxP
-    int compact;                   // 1: compact schedule over used partitions only
+    int num_work;                  // S * KVH * head_groups * maxP (single pass: without maxP)
+    int sched;                     // 0 dense slots, 1 compact list of used partitions, 2 single pass
     int64_t blk_stride;            // bytes per physical block (all kv heads)
     int64_t head_stride;           // bytes per (block, kv head)
     float scale_log2;              // scale * k_scale * log2(e)
@@ -109,6 +109,21 @@ inline bool phase1_compact(int num_seqs) {
     if (PAV2_PHASE1_SCHEDULE == 0) return false;
     if (num_seqs > kMaxCompactSeqs) return false;
     return PAV2_PHASE1_SCHEDULE == 1 || num_seqs > 1;
+}
+
+// Dispatch between the single-pass kernel and the two-phase path: single
+// pass when every sequence fits one partition (no combine needed), or when the
+// (sequence, kv head, head group) workgroups alone fill the chip several
+// times over and the sequences are short enough that walking their
+// partitions in one workgroup does not leave a long tail.  Planned for the
+// MI355X's 256 compute units, without querying the device.
+constexpr int kPlanCUs = 256;
+constexpr int kSinglePassMinRounds = 4;     // workgroups >= this many per CU
+constexpr int kSinglePassMaxPartitions = 8; // and at most this many partitions per sequence
+inline bool prefer_single_pass(int64_t seq_items, int max_num_partitions) {
+    if (max_num_partitions <= 1) return true;
+    return seq_items >= (int64_t)kSinglePassMinRounds * kPlanCUs &&
+           max_num_partitions <= kSinglePassMaxPartitions;
 }
 
 inline int phase1_lds_bytes(int gqa, int head_size, int waves, int bs_log2, int num_seqs, bool compact) {

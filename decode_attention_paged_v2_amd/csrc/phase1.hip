@@ -150,10 +150,15 @@ __device__ __forceinline__ T load_stream(const uint8_t *p) {
         return *reinterpret_cast<const T *>(p);
 }
 
+// SCHED: 0 dense grid of partition slots, 1 compact list of used partitions,
+// 2 single pass (one workgroup per (sequence, kv head, head group) walks all
+// of the sequence's partitions and writes the final output).
 // BS: the block size when fixed at compile time (16 or 32), 0 for any.
-template <int QDT, int KVDT, int D, int WAVES, bool COMPACT, int BS>
+template <int QDT, int KVDT, int D, int WAVES, int SCHED, int BS>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(kPhase1Occupancy)))
 phase1_kernel(const Phase1Params P) {
+    constexpr bool COMPACT = SCHED == 1;
+    constexpr bool SINGLE = SCHED == 2;
     using S = Shape<QDT, KVDT, D>;
     constexpr int NKL = S::kKLoads;
     constexpr int NDT = S::kDTiles;
@@ -187,8 +192,15 @@ phase1_kernel(const Phase1Params P) {
     // Compact schedule: the workgroup computes the exclusive prefix of the
     // sequences' partition counts from seq_lens in LDS and takes a contiguous
     // range of the list of used (seq, partition, kv head, head group) items.
+    // Single pass: the items are the partitions of one (seq, kv head, head
+    // group), blockIdx.x, taken in order.
     int item, item_end;
-    if constexpr (COMPACT) {
+    if constexpr (SINGLE) {
+        if ((int)blockIdx.x >= P.num_work) return;
+        const int L = P.seq_lens[blockIdx.x / (KVH * HG)];
+        item = 0;
+        item_end = L > 0 ? (L + kPartition - 1) / kPartition : 0;
+    } else if constexpr (COMPACT) {
         const int tid = tid0, lane = tid0 & 63, wv = tid0 >> 6;
         const int nthr = WAVES * 64;
         const int per_t = (P.num_seqs + nthr - 1) / nthr;
@@ -234,10 +246,30 @@ phase1_kernel(const Phase1Params P) {
         item_end = item + 1;
     }
 
+    // Single pass: the merging threads carry, per output vector they own, the
+    // running maximum (log2 units, absolute position frame), the rounded-weight
+    // sum and the unnormalised output of the partitions merged so far.
+    constexpr int VEC = QDT == F32 ? 4 : 8;
+    constexpr int PER_HEAD = D / VEC;
+    constexpr int NRUN = SINGLE ? (kMaxHeadsPerGroup * PER_HEAD + WAVES * 64 - 1) / (WAVES * 64) : 1;
+    float run_m[NRUN], run_l[NRUN], run_o[NRUN][VEC];
+#pragma unroll
+    for (int k = 0; k < NRUN; ++k) {
+        run_m[k] = -INFINITY;
+        run_l[k] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) run_o[k][e] = 0.0f;
+    }
+
     for (; item < item_end; ++item) {
     int hg = item % HG;
     int s, g, p;
-    if constexpr (COMPACT) {
+    if constexpr (SINGLE) {
+        hg = blockIdx.x % HG;
+        g = (blockIdx.x / HG) % KVH;
+        s = blockIdx.x / (HG * KVH);
+        p = item;
+    } else if constexpr (COMPACT) {
         int r = item / HG;
         g = r % KVH;
         r /= KVH;
@@ -256,13 +288,13 @@ phase1_kernel(const Phase1Params P) {
         s = w % P.num_seqs;
         p = w / P.num_seqs;
     }
-    if constexpr (COMPACT) __syncthreads();   // the previous item's LDS is free
+    if constexpr (COMPACT || SINGLE) __syncthreads();   // the previous item's LDS is free
 
     // Lane indices.  In the item loop they are taken from an opaque per-item
     // copy of the thread id, so that lane-derived address terms are recomputed
     // per item rather than hoisted out of the loop and kept live across it.
     int tid = tid0;
-    if constexpr (COMPACT) asm volatile("" : "+v"(tid));
+    if constexpr (COMPACT || SINGLE) asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int col = lane & 15;   // token row (K^T loads), head column (outputs), head-dim row (V^T loads)
@@ -273,13 +305,13 @@ phase1_kernel(const Phase1Params P) {
     const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
     const int nh = min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
 
-    if (start >= L) {   // unused partition slot (dense schedule only)
-        if (tid < nh) {
+    if (start >= L) {   // unused partition slot (dense and compact schedules)
+        if (!SINGLE && tid < nh) {
             const int64_t i = ((int64_t)s * P.num_heads + h0 + tid) * maxP + p;
             P.max_logits[i] = -INFINITY;
             P.exp_sums[i] = 0.0f;
         }
-        if constexpr (COMPACT) continue;
+        if constexpr (COMPACT || SINGLE) continue;
         else return;
     }
     const int n_tok = min(kPartition, L - start);
@@ -631,17 +663,16 @@ phase1_kernel(const Phase1Params P) {
     }
     __syncthreads();
 
-    constexpr int VEC = QDT == F32 ? 4 : 8;
-    constexpr int PER_HEAD = D / VEC;
     const float v_scale = P.v_scale;
-    for (int idx = tid; idx < nh * PER_HEAD; idx += WAVES * 64) {
-        const int hh = idx / PER_HEAD;
-        const int d0 = (idx - hh * PER_HEAD) * VEC;
-        float M = -INFINITY;
+    // The wavefronts' (max, sums, unnormalised output) of one output vector,
+    // brought to the largest wavefront maximum.
+    auto combine = [&](int hh, int d0, float &M, float &l, float &lr, float (&a)[VEC]) {
+        M = -INFINITY;
 #pragma unroll
         for (int w2 = 0; w2 < WAVES; ++w2) M = fmaxf(M, s_m[w2 * kMaxHeadsPerGroup + hh]);
         float f[WAVES];
-        float l = 0.0f, lr = 0.0f;
+        l = 0.0f;
+        lr = 0.0f;
 #pragma unroll
         for (int w2 = 0; w2 < WAVES; ++w2) {
             const float mw = s_m[w2 * kMaxHeadsPerGroup + hh];
@@ -649,15 +680,45 @@ phase1_kernel(const Phase1Params P) {
             l += f[w2] * s_l[w2 * kMaxHeadsPerGroup + hh];
             lr += f[w2] * s_lr[w2 * kMaxHeadsPerGroup + hh];
         }
-        const float inv = v_scale / lr;
-        float r[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            float a = 0.0f;
+            float acc = 0.0f;
 #pragma unroll
-            for (int w2 = 0; w2 < WAVES; ++w2) a += f[w2] * s_o[(w2 * heads_alloc + hh) * RS + d0 + e];
-            r[e] = a * inv;
+            for (int w2 = 0; w2 < WAVES; ++w2) acc += f[w2] * s_o[(w2 * heads_alloc + hh) * RS + d0 + e];
+            a[e] = acc;
         }
+    };
+    if constexpr (SINGLE) {
+        // fold this partition into the running state, rescaling whichever
+        // side has the smaller maximum
+#pragma unroll
+        for (int k = 0; k < NRUN; ++k) {
+            const int idx = tid + k * WAVES * 64;
+            if (idx < nh * PER_HEAD) {
+                const int hh = idx / PER_HEAD;
+                const int d0 = (idx - hh * PER_HEAD) * VEC;
+                float M, l, lr, a[VEC];
+                combine(hh, d0, M, l, lr, a);
+                if (P.alibi != nullptr) M += P.alibi[h0 + hh] * kLog2e * (float)last;
+                const float Mn = fmaxf(run_m[k], M);
+                const float fo = exp2_fast(run_m[k] - Mn);   // 0 for the first partition
+                const float fn = exp2_fast(M - Mn);
+                run_m[k] = Mn;
+                run_l[k] = run_l[k] * fo + lr * fn;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) run_o[k][e] = run_o[k][e] * fo + a[e] * fn;
+            }
+        }
+        continue;
+    }
+    for (int idx = tid; idx < nh * PER_HEAD; idx += WAVES * 64) {
+        const int hh = idx / PER_HEAD;
+        const int d0 = (idx - hh * PER_HEAD) * VEC;
+        float M, l, lr, r[VEC];
+        combine(hh, d0, M, l, lr, r);
+        const float inv = v_scale / lr;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) r[e] *= inv;
         const int h = h0 + hh;
         const int64_t srow = (int64_t)s * P.num_heads + h;
         uint8_t *dst = reinterpret_cast<uint8_t *>(P.tmp_out) + ((srow * maxP + p) * D + d0) * QB;
@@ -677,6 +738,33 @@ phase1_kernel(const Phase1Params P) {
     }
         if constexpr (!COMPACT) break;
     }   // item loop
+
+    if constexpr (SINGLE) {   // the normalised output, written once (zero rows for an empty sequence)
+        const int hg = blockIdx.x % HG, g = (blockIdx.x / HG) % KVH, s = blockIdx.x / (HG * KVH);
+        const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
+        const int nh = min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
+#pragma unroll
+        for (int k = 0; k < NRUN; ++k) {
+            const int idx = tid0 + k * WAVES * 64;
+            if (idx < nh * PER_HEAD) {
+                const int hh = idx / PER_HEAD;
+                const int d0 = (idx - hh * PER_HEAD) * VEC;
+                const float inv = run_l[k] > 0.0f ? P.v_scale / run_l[k] : 0.0f;
+                float r[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) r[e] = run_o[k][e] * inv;
+                uint8_t *dst = reinterpret_cast<uint8_t *>(P.tmp_out) +
+                               (((int64_t)s * P.num_heads + h0 + hh) * D + d0) * QB;
+                if constexpr (QDT == F32) {
+                    *reinterpret_cast<f32x4 *>(dst) = f32x4{r[0], r[1], r[2], r[3]};
+                } else {
+                    u32x4 pk = {pack2<QDT>(r[0], r[1]), pack2<QDT>(r[2], r[3]), pack2<QDT>(r[4], r[5]),
+                                pack2<QDT>(r[6], r[7])};
+                    *reinterpret_cast<u32x4 *>(dst) = pk;
+                }
+            }
+        }
+    }
 
     if constexpr (COMPACT) {   // unused slots p >= P_s of this workgroup's share of sequences
         for (int sq = blockIdx.x; sq < P.num_seqs; sq += gridDim.x) {
@@ -706,13 +794,13 @@ int device_cu_count() {
     return cache[dev];
 }
 
-template <int QDT, int KVDT, int D, bool COMPACT, int BS>
+template <int QDT, int KVDT, int D, int SCHED, int BS>
 hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
     constexpr int WAVES = kPhase1Waves;
-    const void *fn = reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, COMPACT, BS>);
+    const void *fn = reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, SCHED, BS>);
     if (lds > 65536) hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     int grid = (p.num_work + 7) / 8 * 8;
-    if (COMPACT) {
+    if (SCHED == 1) {
         // at most kPhase1CompactRounds resident rounds of workgroups, each
         // walking a balanced range of the used items
         int per_cu = 0;
@@ -721,8 +809,10 @@ hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
             per_cu = 1;
         const int cap = kPhase1CompactRounds * device_cu_count() * per_cu;
         grid = grid < cap ? grid : cap;
+    } else if (SCHED == 2) {
+        grid = p.num_work;   // one workgroup per (sequence, kv head, head group)
     }
-    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, COMPACT, BS>), dim3(grid), dim3(WAVES * 64), lds,
+    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, SCHED, BS>), dim3(grid), dim3(WAVES * 64), lds,
                        stream, p);
     return hipGetLastError();
 }
@@ -731,19 +821,23 @@ hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
 // fixed at compile time (load offsets become immediates; the block of a
 // 16-token K tile, and at 32 of a whole unit, is wave-uniform); every other
 // case runs the generic kernel.
-template <int QDT, int KVDT, int D, bool COMPACT>
+template <int QDT, int KVDT, int D, int SCHED>
 hipError_t launch_bs(const Phase1Params &p, int lds, hipStream_t stream) {
     if constexpr (QDT != F32) {
-        if (p.bs_log2 == 4) return launch_sched<QDT, KVDT, D, COMPACT, 16>(p, lds, stream);
-        if (p.bs_log2 == 5) return launch_sched<QDT, KVDT, D, COMPACT, 32>(p, lds, stream);
+        if (p.bs_log2 == 4) return launch_sched<QDT, KVDT, D, SCHED, 16>(p, lds, stream);
+        if (p.bs_log2 == 5) return launch_sched<QDT, KVDT, D, SCHED, 32>(p, lds, stream);
     }
-    return launch_sched<QDT, KVDT, D, COMPACT, 0>(p, lds, stream);
+    return launch_sched<QDT, KVDT, D, SCHED, 0>(p, lds, stream);
 }
 
 template <int QDT, int KVDT, int D>
 hipError_t launch_one(const Phase1Params &p, int lds, hipStream_t stream) {
-    return p.compact ? launch_bs<QDT, KVDT, D, true>(p, lds, stream)
-                     : launch_bs<QDT, KVDT, D, false>(p, lds, stream);
+    switch (p.sched) {
+    case 0: return launch_bs<QDT, KVDT, D, 0>(p, lds, stream);
+    case 1: return launch_bs<QDT, KVDT, D, 1>(p, lds, stream);
+    case 2: return launch_bs<QDT, KVDT, D, 2>(p, lds, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int QDT, int KVDT>

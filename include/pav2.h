@@ -112,7 +112,36 @@ int pav2_paged_attention_v2(
     pav2_stream_t stream);
 
 /*
- * Phase 1 alone (same arguments as above without `output`): writes
+ * PagedAttention V1, the single-pass variant (page "paged_attn.py",
+ * forward_decode, which calls it when every sequence fits one partition or
+ * when the sequence x head parallelism already fills the device): the same
+ * output as pav2_paged_attention_v2, from one launch and with no partition
+ * workspace.  One workgroup per (sequence, kv head, group of up to 16 query
+ * heads) walks the sequence's 512-token partitions in order, folding each
+ * into a running (max, weight sum, weighted output) with the combine of the
+ * pages' cross-partition reduction, and writes the normalised output once.
+ *
+ * Arguments as the pages' V1 op (output, query, key_cache, value_cache,
+ * num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+ * alibi_slopes, kv_cache_dtype, k_scale, v_scale), then the shapes, the query
+ * dtype and the stream.  Supported combinations as for V2; there is no
+ * partition-count limit beyond max_seq_len <= 16384 * 512.
+ */
+int pav2_paged_attention_v1(
+    void *output,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_kv_heads, float scale,
+    const int32_t *block_tables, const int32_t *seq_lens,
+    int block_size, int max_seq_len,
+    const float *alibi_slopes,
+    pav2_dtype_t kv_cache_dtype, float k_scale, float v_scale,
+    int num_seqs, int num_heads, int head_size, int num_blocks,
+    int max_blocks_per_seq,
+    pav2_dtype_t query_dtype,
+    pav2_stream_t stream);
+
+/*
+ * Phase 1 alone (same arguments as pav2_paged_attention_v2 without `output`): writes
  * exp_sums, max_logits and tmp_output.
  */
 int pav2_phase1(
@@ -151,6 +180,11 @@ typedef struct {
     int phase2_lds_bytes;
     int phase1_compact;       /* 1: phase 1 walks a compact list of used partitions
                                  (grid: min(phase1_workgroups, 8 resident rounds)) */
+    int use_v1;               /* 1: the single-pass entry point is the faster choice
+                                 (every sequence in one partition, or enough
+                                 (sequence, kv head) work to fill the chip) */
+    int v1_workgroups;        /* single-pass grid: num_seqs * num_kv_heads * head_groups */
+    int v1_lds_bytes;         /* dynamic LDS per single-pass workgroup */
 } pav2_plan_t;
 
 int pav2_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size,

@@ -90,6 +90,45 @@ def test_zero_sequences_is_a_no_op():
     assert pav2.last_error() == ""
 
 
+def _call_v1(**over):
+    """pav2_paged_attention_v1 with host-only pointers and overridable sizes."""
+    lib = pav2.load()
+    a = dict(output=ctypes.c_void_p(16), query=ctypes.c_void_p(16), key_cache=ctypes.c_void_p(16),
+             value_cache=ctypes.c_void_p(16), num_kv_heads=4, scale=0.0625,
+             block_tables=ctypes.c_void_p(16), seq_lens=ctypes.c_void_p(16), block_size=16,
+             max_seq_len=100000, alibi_slopes=None, kv_cache_dtype=B.BF16, k_scale=1.0, v_scale=1.0,
+             num_seqs=4, num_heads=24, head_size=256, num_blocks=25000, max_blocks_per_seq=6250,
+             query_dtype=B.BF16, stream=None)
+    a.update(over)
+    return lib.pav2_paged_attention_v1(*a.values())
+
+
+V1_INVALID = [
+    (dict(num_heads=25), -1, "multiple of num_kv_heads"),
+    (dict(head_size=100), -2, "head_size 100"),
+    (dict(block_size=24), -1, "block_size 24"),
+    (dict(max_blocks_per_seq=6249), -1, "max_blocks_per_seq"),
+    (dict(query_dtype=B.F16), -2, "query dtype f16 with kv dtype bf16"),
+    (dict(output=None), -1, "NULL"),
+    (dict(seq_lens=None), -1, "NULL"),
+    (dict(v_scale=float("nan")), -1, "finite"),
+    (dict(max_seq_len=-1), -1, "max_seq_len"),
+    (dict(max_seq_len=16385 * 512, max_blocks_per_seq=16385 * 32), -2, "exceeds"),
+]
+
+
+@pytest.mark.parametrize("over,status,msg", V1_INVALID)
+def test_v1_invalid_arguments_are_rejected(over, status, msg):
+    assert _call_v1(**over) == status
+    assert msg in pav2.last_error()
+
+
+def test_v1_zero_sequences_is_a_no_op():
+    assert _call_v1(num_seqs=0, output=None, query=None) == 0
+    assert _call_v1(num_seqs=0, max_seq_len=0) == 0
+    assert pav2.last_error() == ""
+
+
 def test_phase2_validation():
     lib = pav2.load()
     v = ctypes.c_void_p(16)
@@ -140,8 +179,28 @@ def test_plan(cfg, expect):
         assert p[k] == v, (k, p)
     assert p["phase1_threads"] == 256 and p["phase2_threads"] in (256, 1024)
     assert p["phase1_compact"] == (1 if cfg["num_seqs"] > 1 else 0)
+    assert p["use_v1"] == 0
+    assert p["v1_workgroups"] == cfg["num_seqs"] * cfg["num_kv_heads"] * p["head_groups"]
+    assert p["v1_lds_bytes"] <= p["phase1_lds_bytes"]
     assert 0 < p["phase1_lds_bytes"] <= 160 * 1024
     assert p["phase2_lds_bytes"] == 0
+
+
+@pytest.mark.parametrize("num_seqs,num_kv_heads,maxp,expect", [
+    (1, 4, 1, 1),       # one partition: no combine needed
+    (4, 4, 1, 1),
+    (256, 8, 4, 1),     # 2048 (seq, kv head) workgroups, 4 partitions each
+    (128, 8, 8, 1),     # 1024 workgroups = 4 per compute unit
+    (127, 8, 8, 0),     # just under 4 per compute unit
+    (256, 8, 9, 0),     # more than 8 partitions per sequence
+    (4, 4, 196, 0),     # long context
+])
+def test_plan_v1_choice(num_seqs, num_kv_heads, maxp, expect):
+    """Single pass when every sequence fits one partition, or when the (seq, kv
+    head, head group) workgroups fill the 256 compute units 4 times over and
+    sequences span at most 8 partitions."""
+    p = pav2.plan(num_seqs, 8 * num_kv_heads, num_kv_heads, 128, 16, maxp, B.BF16, B.BF16)
+    assert p["use_v1"] == expect
 
 
 def test_python_binding_has_no_cpu_path():

@@ -40,3 +40,5 @@ def test_long_context_workload_bytes():
     # tmp rows of 196 partitions per (seq, head) and two float32 statistics per slot
     assert b["phase1_write"] == 4 * 24 * 196 * 256 * 2 + 8 * 4 * 24 * 196
     assert b["phase1"] == b["phase1_read"] + b["phase1_write"]
+    # the single pass reads the same and writes only the output rows
+    assert b["v1"] == b["phase1_read"] + 4 * 24 * 256 * 2
