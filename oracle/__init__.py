@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline leg may import this package; the product library never does.  It
 shares no code with the HIP path.
 
-The arithmetic lives in ``pav2_oracle.c`` (plain C, float64), which follows
+The arithmetic lives in ``pav2_oracle.c`` (plain C, float64; the KV-cache
+write in float32, its working precision), which follows
 the page "paged_attention_v2_pytorch.py" (function paged_attention_v2_pytorch)
 step by step; see that file's header for the steps and for the one reading
 taken (partition outputs are normalised by their own exp-sum).  This module
@@ -74,6 +75,14 @@ def _load():
                 F, F, F,
                 P, I]
             lib.oracle_dense_attention.restype = I
+            lib.oracle_encode.argtypes = [I, P, ctypes.c_int64, P]
+            lib.oracle_encode.restype = I
+            lib.oracle_reshape_and_cache.argtypes = [
+                P, P, P, P,            # key, value, key_cache, value_cache
+                P, I, F, F,            # slot_mapping, cache_dtype, k_scale, v_scale
+                I, I, I, I,            # num_tokens, num_kv_heads, head_size, block_size
+                ctypes.c_int64, I]     # num_blocks, input dtype
+            lib.oracle_reshape_and_cache.restype = I
             _lib = lib
     return _lib
 
@@ -193,3 +202,39 @@ def dense_attention(query, key_cache, value_cache, block_tables, seq_lens, *,
     if rc != 0:
         raise ValueError(f"oracle_dense_attention rejected its arguments (rc={rc})")
     return out
+
+
+def encode(dtype: int, values) -> np.ndarray:
+    """Round float32 values to elements of the given dtype code (raw element bytes)."""
+    src = np.ascontiguousarray(np.asarray(values, dtype=np.float32).ravel())
+    out = np.empty(src.size * ELEM_SIZE[dtype], dtype=np.uint8)
+    if _load().oracle_encode(dtype, _ptr(src), src.size, _ptr(out)) != 0:
+        raise ValueError("oracle_encode failed")
+    return out
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, block_size,
+                      cache_dtype, k_scale=1.0, v_scale=1.0):
+    """KV-cache write: key, value [T, kv_h, d] into copies of the paged caches.
+
+    key_cache [NB, kv_h, d/x, block_size, x], value_cache [NB, kv_h, d,
+    block_size] are torch tensors or numpy arrays of raw element bytes; the
+    caches are not modified.  Returns the written (key_cache, value_cache) as
+    numpy arrays of the caches' raw elements (float32; int16 for 16-bit
+    formats; uint8 for fp8), in the caches' shapes.
+    """
+    k = _raw(key)
+    v = _raw(value)
+    kc = np.array(_raw(key_cache), copy=True)
+    vc = np.array(_raw(value_cache), copy=True)
+    sm = np.ascontiguousarray(np.asarray(slot_mapping.cpu() if hasattr(slot_mapping, "cpu") else slot_mapping,
+                                         dtype=np.int64))
+    T, KVH, D = (int(n) for n in key.shape)
+    nb = int(key_cache.shape[0])
+    in_dtype = dtype_code(key.dtype)
+    rc = _load().oracle_reshape_and_cache(
+        _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(sm), int(cache_dtype), float(k_scale),
+        float(v_scale), T, KVH, D, int(block_size), nb, in_dtype)
+    if rc != 0:
+        raise ValueError(f"oracle_reshape_and_cache rejected its arguments (rc={rc})")
+    return kc, vc

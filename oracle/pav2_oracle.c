@@ -41,6 +41,7 @@
  * binary32), and OCP 8-bit E4M3 ("e4m3fn": bias 7, no infinities, S.1111.111
  * is NaN).
  */
+#include <fenv.h>
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
@@ -350,4 +351,131 @@ int oracle_dense_attention(
     P.scale = scale; P.k_scale = k_scale; P.v_scale = v_scale;
     P.out = out; P.pair_mask = pair_mask; P.dense = 1;
     return run(&P, num_threads);
+}
+
+/* ---- KV-cache write ----------------------------------------------------
+ *
+ * Page "paged_attn.py", write_to_paged_cache: the new tokens' keys and values
+ * enter the paged cache through reshape_and_cache(key, value, key_cache,
+ * value_cache, slot_mapping, kv_cache_dtype, k_scale, v_scale).  The page
+ * shows the call, not its body; the reading taken here is the inverse of the
+ * decode gather above (step 2):
+ *
+ *   slot = slot_mapping[t]; a negative slot means "no slot" and the token is
+ *   skipped; block = slot / block_size, offset = slot % block_size;
+ *   key_cache  [block, g, i / x, offset, i % x] = enc(key  [t, g, i] / k_scale)
+ *   value_cache[block, g, i,     offset]        = enc(value[t, g, i] / v_scale)
+ *
+ * with x = 16 / element size of the cache dtype (split_kv_cache on the same
+ * page).  Decode multiplies by k_scale / v_scale (step 2), so the write
+ * divides.  The quotient is taken in float32 (the cache write's working
+ * precision, as the scales are float32 arguments), then rounded to the cache
+ * dtype to nearest, ties to even.  The cache dtype is the input dtype
+ * ("auto") or OCP E4M3; E4M3 saturates at +-448 (it has no infinities), NaN
+ * stays NaN.  The encoders below are written from the formats' definitions.
+ */
+
+/* Round a > 0 to a binary format with `frac` fraction bits, minimum normal
+ * exponent emin, maximum exponent emax and exponent bias `bias` (round to
+ * nearest, ties to even: nearbyint in the default rounding mode); returns the
+ * code without its sign bit, or -1 when the rounded value overflows. */
+static int64_t round_to_format(double a, int frac, int emin, int emax, int bias) {
+    if (a == 0.0) return 0;
+    int e2;
+    frexp(a, &e2);                          /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;
+    if (E < emin) {                         /* subnormal grid: multiples of 2^(emin - frac) */
+        double m = nearbyint(ldexp(a, frac - emin));
+        return (int64_t)m;                  /* m == 2^frac is the smallest normal's code */
+    }
+    double m = nearbyint(ldexp(a, frac - E));   /* in [2^frac, 2^(frac+1)] */
+    if (m == ldexp(1.0, frac + 1)) {
+        m = ldexp(1.0, frac);
+        E += 1;
+    }
+    if (E > emax) return -1;
+    return ((int64_t)(E + bias) << frac) | ((int64_t)m - ((int64_t)1 << frac));
+}
+
+static uint16_t enc_f16(float f) {
+    double v = (double)f;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v)) return sign | 0x7e00;
+    double a = fabs(v);
+    if (isinf(a)) return sign | 0x7c00;
+    int64_t c = round_to_format(a, 10, -14, 15, 15);
+    return c < 0 ? (uint16_t)(sign | 0x7c00) : (uint16_t)(sign | c);
+}
+
+static uint16_t enc_bf16(float f) {
+    double v = (double)f;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v)) return sign | 0x7fc0;
+    double a = fabs(v);
+    if (isinf(a)) return sign | 0x7f80;
+    int64_t c = round_to_format(a, 7, -126, 127, 127);
+    return c < 0 ? (uint16_t)(sign | 0x7f80) : (uint16_t)(sign | c);
+}
+
+static uint8_t enc_fp8_e4m3(float f) {
+    double v = (double)f;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    if (isnan(v)) return sign | 0x7f;
+    double a = fabs(v);
+    if (a > 448.0) a = 448.0;               /* saturate (also infinities) */
+    int64_t c = round_to_format(a, 3, -6, 8, 7);
+    return (uint8_t)(sign | c);             /* c <= 0x7e after saturation */
+}
+
+static void store_elem(int dtype, void *base, int64_t idx, float f) {
+    uint8_t *p = (uint8_t *)base;
+    switch (dtype) {
+    case OR_F32: memcpy(p + 4 * idx, &f, 4); break;
+    case OR_F16: { uint16_t b = enc_f16(f); memcpy(p + 2 * idx, &b, 2); break; }
+    case OR_BF16: { uint16_t b = enc_bf16(f); memcpy(p + 2 * idx, &b, 2); break; }
+    case OR_FP8_E4M3: p[idx] = enc_fp8_e4m3(f); break;
+    default: break;
+    }
+}
+
+/* Encode n float32 values into elements of `dtype` (exposed so tests can
+ * check the encoders against library conversions). */
+int oracle_encode(int dtype, const float *src, int64_t n, void *dst) {
+    if (elem_size(dtype) == 0) return -1;
+    fesetround(FE_TONEAREST);
+    for (int64_t i = 0; i < n; ++i) store_elem(dtype, dst, i, src[i]);
+    return 0;
+}
+
+int oracle_reshape_and_cache(
+    const void *key, const void *value, void *key_cache, void *value_cache,
+    const int64_t *slot_mapping, int cache_dtype, float k_scale, float v_scale,
+    int num_tokens, int num_kv_heads, int head_size, int block_size,
+    int64_t num_blocks, int in_dtype) {
+    if (in_dtype == OR_FP8_E4M3 || elem_size(in_dtype) == 0 || elem_size(cache_dtype) == 0) return -1;
+    if (cache_dtype != in_dtype && cache_dtype != OR_FP8_E4M3) return -1;
+    int x = 16 / elem_size(cache_dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || head_size % x != 0 || block_size <= 0)
+        return -1;
+    for (int t = 0; t < num_tokens; ++t)
+        if (slot_mapping[t] >= num_blocks * (int64_t)block_size) return -1;
+    fesetround(FE_TONEAREST);
+    int64_t d = head_size, kvh = num_kv_heads, bs = block_size;
+    for (int t = 0; t < num_tokens; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        int64_t blk = slot / bs, off = slot % bs;
+        for (int64_t g = 0; g < kvh; ++g) {
+            for (int64_t i = 0; i < d; ++i) {
+                int64_t src = ((int64_t)t * kvh + g) * d + i;
+                float kq = (float)dec(in_dtype, key, src) / k_scale;
+                float vq = (float)dec(in_dtype, value, src) / v_scale;
+                int64_t kidx = (((blk * kvh + g) * (d / x) + i / x) * bs + off) * x + i % x;
+                int64_t vidx = ((blk * kvh + g) * d + i) * bs + off;
+                store_elem(cache_dtype, key_cache, kidx, kq);
+                store_elem(cache_dtype, value_cache, vidx, vq);
+            }
+        }
+    }
+    return 0;
 }
