@@ -107,6 +107,106 @@ def measured_traffic(config, entry="v2"):
     return round(float(data["phase1_traffic_bytes"]))
 
 
+def _time_launches(fn, steps, warmup, stream):
+    """Mean / min event time (ms) of fn() launches on `stream`, and wall ms per launch."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return float(np.mean(ms)), float(np.min(ms)), wall
+
+
+def cache_write_cpu_baseline(wl, target_core_seconds=10.0):
+    """The oracle's cache write on a bounded sample of the workload's tokens (one thread)."""
+    import oracle
+    T = wl.key.shape[0]
+    kvh, d = wl.key.shape[1], wl.key.shape[2]
+    bs = wl.value_cache.shape[3]
+    code = oracle.dtype_code(wl.cache_dtype)
+
+    def run(n):
+        k, v = wl.key[:n].cpu(), wl.value[:n].cpu()
+        nb = (n + bs - 1) // bs
+        kc = torch.empty((nb,) + tuple(wl.key_cache.shape[1:]), dtype=wl.key_cache.dtype)
+        vc = torch.empty((nb,) + tuple(wl.value_cache.shape[1:]), dtype=wl.value_cache.dtype)
+        t0 = time.perf_counter()
+        oracle.reshape_and_cache(k, v, kc, vc, torch.arange(n), block_size=bs, cache_dtype=code,
+                                 k_scale=wl.k_scale, v_scale=wl.v_scale)
+        return time.perf_counter() - t0
+    n0 = min(T, 256)
+    per_tok = max(1e-7, run(n0) / n0)
+    n = int(max(1, min(T, target_core_seconds / per_tok)))
+    dt = run(n)
+    bytes_ = n * kvh * d * 2 * (wl.key.element_size() + wl.key_cache.element_size())
+    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {T} tokens ({bytes_ / 1e6:.1f} MB moved), C oracle, {dt:.2f} s wall",
+            "seconds": round(dt, 3)}
+
+
+def cache_write_bench(args, dev):
+    """KV-cache write: the whole context of the workload as one launch (the
+    prefill of every sequence), and the decode step's one token per sequence."""
+    pav2.load()
+    spec = W.SPECS[args.config]
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for kind in ("prefill", "decode_step"):
+        wl = W.cache_write_workload(spec, dev, decode_step=kind == "decode_step")
+        kvdt = "fp8_e4m3" if wl.cache_dtype == torch.float8_e4m3fn else "auto"
+        fn = lambda: pav2.reshape_and_cache(wl.key, wl.value, wl.key_cache, wl.value_cache, wl.slot_mapping,
+                                            kvdt, wl.k_scale, wl.v_scale)
+        mean, mn, wall = _time_launches(fn, args.steps, args.warmup, stream)
+        res[kind] = {"tokens": int(wl.key.shape[0]), "bytes_moved": wl.bytes_moved(),
+                     "ms_mean": round(mean, 5), "ms_min": round(mn, 5), "wall_ms_per_launch": round(wall, 5),
+                     "GBps": round(wl.bytes_moved() / (mean * 1e-3) / 1e9, 2)}
+        if kind == "prefill":
+            big = wl
+        else:
+            del wl
+    p = res["prefill"]
+    achieved = p["bytes_moved"] / (p["ms_mean"] * 1e-3) / 1e9
+    result = {
+        "metric": "KV-cache write GB/s (input read + cache written) and % of HBM peak",
+        "value": round(achieved, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": p["ms_mean"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE_NAME[big.key.dtype] + ("->fp8_e4m3" if big.cache_dtype == torch.float8_e4m3fn else ""),
+        "data": "synthetic",
+        "config": {"workload": f"{args.config} context written through its block tables: {DESCR[args.config]}",
+                   "tokens": p["tokens"]},
+        "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "prefill": p, "decode_step": res["decode_step"],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_cache_traffic(args.config),
+                     "kernel": "cache_write_kernel", "algorithmic_bytes_per_launch": p["bytes_moved"]},
+        "library": pav2.lib_path(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cache_write_cpu_baseline(big)
+    return result
+
+
+def measured_cache_traffic(config):
+    """HBM bytes per cache-write launch from the committed counter summary, or
+    None when there is none or it was taken on different kernel sources."""
+    from decode_attention_paged_v2_amd import rocprof_harness
+    path = os.path.join(ROOT, "profiles", f"cache_write_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    if data.get("source_hash") != rocprof_harness.source_hash("cache_write") or "traffic_bytes" not in data:
+        return None
+    return round(float(data["traffic_bytes"]))
+
+
 def copy_reference(dev, steps, warmup, nbytes=1 << 30):
     """A plain device-to-device copy of nbytes: reads nbytes, writes nbytes."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
@@ -137,9 +237,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="extra per-step timings with a 1 GiB cache flush before each step")
-    ap.add_argument("--mode", default="decode", choices=["decode", "copy"],
+    ap.add_argument("--mode", default="decode", choices=["decode", "copy", "cache_write"],
                     help="copy: time a plain 1 GiB device copy (the reference kernel for "
-                         "scaling HBM byte counters and for achievable bandwidth)")
+                         "scaling HBM byte counters and for achievable bandwidth); cache_write: "
+                         "time the KV-cache write of the workload's whole context (and of one "
+                         "decode step's tokens)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -154,6 +256,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.mode == "copy":
         print(json.dumps(copy_reference(dev, args.steps, args.warmup)), flush=True)
+        return
+    if args.mode == "cache_write":
+        print(json.dumps(cache_write_bench(args, dev)), flush=True)
         return
     pav2.load()
     spec = W.SPECS[args.config]

@@ -8,5 +8,5 @@ loaded on first use; there is no CPU fallback.
 from ._binding import (  # noqa: F401
     BF16, F16, F32, FP8_E4M3, PARTITION_SIZE, Pav2Error, check_inputs, decode, decode_kv, forward_decode,
     last_error, lib_path, load, max_num_partitions, paged_attention_v1, paged_attention_v2, phase1, phase2,
-    plan, version,
+    plan, reshape_and_cache, version,
 )

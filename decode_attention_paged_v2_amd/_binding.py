@@ -64,6 +64,8 @@ def load():
         L.pav2_plan.restype = I
         L.pav2_decode_kv.argtypes = [P, P, ctypes.c_int64, I, I, P]
         L.pav2_decode_kv.restype = I
+        L.pav2_reshape_and_cache.argtypes = [P, P, P, P, P, I, F, F, I, I, I, I, I, I, P]
+        L.pav2_reshape_and_cache.restype = I
         L.pav2_check_inputs.argtypes = [P, P, I, I, I, I, P, P]
         L.pav2_check_inputs.restype = I
         L.pav2_max_num_partitions.argtypes = [I]
@@ -232,6 +234,30 @@ def decode_kv(src, compute_dtype=None, stream=None):
                                _stream(src, stream))
     _check(rc)
     return dst.view(src.shape)
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, kv_cache_dtype="auto",
+                      k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """KV-cache write (pav2_reshape_and_cache): key, value [T, kv_h, d] into the
+    paged caches at slot_mapping [T] (int64; negative = no slot)."""
+    import torch
+    T, KVH, D = (int(v) for v in key.shape)
+    if tuple(value.shape) != (T, KVH, D) or value.dtype != key.dtype:
+        raise ValueError("value must match key in shape and dtype")
+    if key_cache.dim() != 5 or value_cache.dim() != 4:
+        raise ValueError("key_cache must be 5-D and value_cache 4-D")
+    NB, bs = int(value_cache.shape[0]), int(value_cache.shape[3])
+    if int(key_cache.shape[0]) != NB or int(key_cache.shape[1]) != KVH or int(value_cache.shape[1]) != KVH \
+            or int(value_cache.shape[2]) != D or int(key_cache.shape[3]) != bs:
+        raise ValueError("cache shapes disagree with key [num_tokens, num_kv_heads, head_size]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    kvdt = _dtype_code(key_cache, kv_cache_dtype)
+    rc = load().pav2_reshape_and_cache(
+        _dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(slot_mapping.reshape(-1), "slot_mapping"), kvdt, float(k_scale), float(v_scale), T, KVH, D, bs, NB,
+        _dtype_code(key), _stream(key, stream))
+    _check(rc)
 
 
 def check_inputs(block_tables, seq_lens, block_size, num_blocks, stream=None) -> dict:

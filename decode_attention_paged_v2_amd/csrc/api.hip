@@ -363,6 +363,56 @@ int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype
                          "decode_kv");
 }
 
+int pav2_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,
+                           const int64_t *slot_mapping, pav2_dtype_t kv_cache_dtype, float k_scale,
+                           float v_scale, int num_tokens, int num_kv_heads, int head_size, int block_size,
+                           int num_blocks, pav2_dtype_t input_dtype, pav2_stream_t stream) {
+    g_err[0] = 0;
+    if (num_tokens < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (num_kv_heads <= 0 || num_blocks <= 0)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "num_kv_heads (%d) and num_blocks (%d) must be > 0", num_kv_heads,
+                    num_blocks);
+    if (input_dtype != PAV2_F32 && input_dtype != PAV2_F16 && input_dtype != PAV2_BF16)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "input dtype must be f32, f16 or bf16 (got %d)", (int)input_dtype);
+    if (kv_cache_dtype != input_dtype && kv_cache_dtype != PAV2_FP8_E4M3)
+        return fail(PAV2_ERR_UNSUPPORTED, "kv_cache_dtype %s must be the input dtype %s or fp8_e4m3",
+                    dt_name(kv_cache_dtype), dt_name(input_dtype));
+    if (!supported_head_size(head_size))
+        return fail(PAV2_ERR_UNSUPPORTED, "head_size %d is not one of 64, 80, 96, 112, 120, 128, 192, 256",
+                    head_size);
+    const int x = 16 / elem_bytes(kv_cache_dtype);
+    if (head_size % x != 0)
+        return fail(PAV2_ERR_UNSUPPORTED, "head_size %d is not a multiple of x = %d for %s", head_size, x,
+                    dt_name(kv_cache_dtype));
+    const int bs_log2 = ilog2_exact(block_size);
+    if (bs_log2 < 3 || bs_log2 > 9)
+        return fail(PAV2_ERR_UNSUPPORTED, "block_size %d must be a power of two in [8, 512]", block_size);
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale))
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "k_scale (%g) and v_scale (%g) must be finite and > 0",
+                    (double)k_scale, (double)v_scale);
+    if (num_tokens == 0) return PAV2_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    pav2::CacheParams p;
+    p.key = static_cast<const uint8_t *>(key);
+    p.value = static_cast<const uint8_t *>(value);
+    p.key_cache = static_cast<uint8_t *>(key_cache);
+    p.value_cache = static_cast<uint8_t *>(value_cache);
+    p.slot_mapping = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_kv_heads = num_kv_heads;
+    p.head_size = head_size;
+    p.bs_log2 = bs_log2;
+    p.num_slots = (int64_t)num_blocks << bs_log2;
+    p.head_stride = (int64_t)head_size * block_size * elem_bytes(kv_cache_dtype);
+    p.blk_stride = p.head_stride * num_kv_heads;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    return launch_status(pav2::launch_cache_write(p, (int)input_dtype, (int)kv_cache_dtype,
+                                                  static_cast<hipStream_t>(stream)),
+                         "reshape_and_cache");
+}
+
 int pav2_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
                       int max_blocks_per_seq, int block_size, int num_blocks, int64_t *report,
                       pav2_stream_t stream) {

@@ -36,12 +36,15 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 BENCH = os.path.join(ROOT, "bench.py")
-KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("phase1.hip", "phase2.hip", "pav2_internal.h")]
+KERNEL_SOURCES = {
+    "decode": [os.path.join(HERE, "csrc", f) for f in ("phase1.hip", "phase2.hip", "pav2_internal.h")],
+    "cache_write": [os.path.join(HERE, "csrc", f) for f in ("cache.hip", "pav2_internal.h")],
+}
 
 
-def source_hash() -> str:
+def source_hash(mode: str = "decode") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[mode]:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -78,20 +81,38 @@ def _kind(name: str) -> str:
         return "phase1"
     if "phase2_kernel" in name:
         return "phase2"
+    if "cache_write_kernel" in name:
+        return "cache_write"
     return "other"
 
 
-def kernel_trace(config: str, out: str, steps: int = 10) -> dict:
-    d = os.path.join(out, f"trace_{config}")
+def _bench_args(config: str, mode: str, steps: int, warmup: int) -> list:
+    args = [sys.executable, BENCH, "--config", config, "--steps", str(steps), "--warmup", str(warmup),
+            "--no-cpu-baseline"]
+    return args + (["--mode", "cache_write"] if mode == "cache_write" else ["--flush-steps", "0"])
+
+
+def kernel_trace(config: str, out: str, steps: int = 10, mode: str = "decode") -> dict:
+    d = os.path.join(out, f"trace_{mode}_{config}")
     shutil.rmtree(d, ignore_errors=True)
-    bench = [sys.executable, BENCH, "--config", config, "--steps", str(steps), "--warmup", "2",
-             "--no-cpu-baseline", "--flush-steps", "0"]
+    bench = _bench_args(config, mode, steps, 2)
     cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", d, "-o", "run", "--output-format", "csv",
            "--"] + bench
-    _run(cmd, os.path.join(out, f"trace_{config}.log"), 300)
+    _run(cmd, os.path.join(out, f"trace_{mode}_{config}.log"), 300)
     rel = os.path.relpath(d, ROOT)
     res = {"command": " ".join(["rocprofv3", "--kernel-trace", "--stats", "-d", rel, "-o", "run",
                                 "--output-format", "csv", "--", "python3", "bench.py"] + bench[2:])}
+    if mode == "cache_write":
+        # the bench times the whole-context write and a decode step's write with
+        # the same kernel: keep the dispatches of the largest grid (the former)
+        rows = [r for r in _csv(os.path.join(d, "**", "run_kernel_trace.csv"))
+                if _kind(r["Kernel_Name"]) == "cache_write"]
+        size = lambda r: int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"])
+        top = max(size(r) for r in rows)
+        us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if size(r) == top]
+        res["cache_write"] = {"name": rows[0]["Kernel_Name"], "calls": len(us), "avg_us": sum(us) / len(us),
+                              "min_us": min(us), "max_us": max(us), "grid": top}
+        return res
     for r in _csv(os.path.join(d, "**", "run_kernel_stats.csv")):
         k = _kind(r["Name"])
         if k == "other":
@@ -101,21 +122,21 @@ def kernel_trace(config: str, out: str, steps: int = 10) -> dict:
     return res
 
 
-def pmc(config: str, out: str) -> dict:
-    """FETCH_SIZE and WRITE_SIZE per phase-1 launch, scaled by the copy reference."""
+def pmc(config: str, out: str, mode: str = "decode") -> dict:
+    """FETCH_SIZE and WRITE_SIZE per launch of the profiled kernels, scaled by the copy reference."""
     res = {}
+    kinds = ("phase1", "phase2") if mode == "decode" else ("cache_write",)
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         for what in (config, "copy"):
-            d = os.path.join(out, f"pmc_{counter}_{what}")
+            d = os.path.join(out, f"pmc_{counter}_{what if what == 'copy' else mode + '_' + what}")
             shutil.rmtree(d, ignore_errors=True)
             if what == "copy":
                 bench = [sys.executable, BENCH, "--mode", "copy", "--steps", "3", "--warmup", "1"]
             else:
-                bench = [sys.executable, BENCH, "--config", what, "--steps", "3", "--warmup", "1",
-                         "--no-cpu-baseline", "--flush-steps", "0"]
+                bench = _bench_args(what, mode, 3, 1)
             cmd = ["rocprofv3", "--pmc", counter, "-d", d, "-o", "run", "--output-format", "csv",
                    "--"] + bench
-            _run(cmd, os.path.join(out, f"pmc_{counter}_{what}.log"), 120)
+            _run(cmd, d + ".log", 120)
             rows = _csv(os.path.join(d, "**", "run_counter_collection.csv"))
             if what == "copy":
                 vals = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
@@ -123,10 +144,13 @@ def pmc(config: str, out: str) -> dict:
                 res[f"{counter}_copy_kib"] = sum(vals) / len(vals)
                 res[f"{counter}_scale"] = (1 << 30) / 1024.0 / res[f"{counter}_copy_kib"]
             else:
-                for k in ("phase1", "phase2"):
-                    vals = [float(r["Counter_Value"]) for r in rows if _kind(r["Kernel_Name"]) == k]
+                for k in kinds:
+                    # dispatches of the largest grid (the cache write also times a decode step)
+                    mine = [r for r in rows if _kind(r["Kernel_Name"]) == k]
+                    top = max(int(r["Grid_Size"]) for r in mine)
+                    vals = [float(r["Counter_Value"]) for r in mine if int(r["Grid_Size"]) == top]
                     res[f"{counter}_{k}_kib"] = sum(vals) / len(vals)
-    for k in ("phase1", "phase2"):
+    for k in kinds:
         res[f"{k}_fetch_bytes"] = res[f"FETCH_SIZE_{k}_kib"] * 1024 * res["FETCH_SIZE_scale"]
         res[f"{k}_write_bytes"] = res[f"WRITE_SIZE_{k}_kib"] * 1024 * res["WRITE_SIZE_scale"]
     return res
@@ -238,9 +262,58 @@ def write_summary(config: str, out: str, trace: dict, counters: dict | None, sqv
     return os.path.join(out, name + ".md")
 
 
+def write_cache_summary(config: str, out: str, trace: dict, counters: dict | None) -> str:
+    from . import workloads
+    import torch
+    sp = workloads.SPECS[config]
+    gl = torch.Generator()
+    gl.manual_seed(sp.seed)
+    tokens = sum(int(v) for v in sp.lens(gl))
+    eb = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+    rd = tokens * sp.num_kv_heads * sp.head_size * 2 * eb[sp.q_dtype]   # key and value read
+    alg = rd + tokens * sp.num_kv_heads * sp.head_size * 2 * eb[sp.kv_dtype]
+    t = trace["cache_write"]
+    gbps = alg / (t["avg_us"] * 1e-6) / 1e9
+    name = "cache_write_" + config
+    lines = [f"# KV-cache write profile: {config} (whole context in one launch)", "",
+             f"Kernel sources hash: `{source_hash('cache_write')}`", "",
+             "Command (from the repository root):", "",
+             "    python -m decode_attention_paged_v2_amd.rocprof_harness --mode cache_write --config "
+             f"{config} --out gpurun_out/prof{' --pmc' if counters else ''}", "",
+             "which runs:", "", "    " + trace["command"], "",
+             "Dispatches of the largest grid (the whole-context write; the bench also times a decode "
+             "step's write with the same kernel), from the kernel trace:", "",
+             "| kernel | grid | calls | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|---|",
+             f"| `{t['name'][:90]}` | {t['grid']} | {t['calls']} | {t['avg_us']:.2f} | {t['min_us']:.2f} | "
+             f"{t['max_us']:.2f} |", "",
+             f"Algorithmic bytes per launch (input read + cache written): {alg:,}; at the average "
+             f"duration that is {gbps:.1f} GB/s = {100 * gbps / 8000:.1f} % of 8 TB/s."]
+    data = {"config": config, "source_hash": source_hash("cache_write"), "trace": trace,
+            "algorithmic_bytes": alg, "achieved_GBps": gbps, "taken": time.strftime("%Y-%m-%d %H:%M:%S")}
+    if counters:
+        f1, w1 = counters["cache_write_fetch_bytes"], counters["cache_write_write_bytes"]
+        data["counters"] = counters
+        data["traffic_bytes"] = f1 + w1
+        lines += ["", "HBM counters (`rocprofv3 --pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, each over the "
+                      "same bench command and over `bench.py --mode copy`, a 1 GiB copy):", "",
+                  "| quantity | value |", "|---|---|",
+                  f"| scale factors (known / counted) | fetch {counters['FETCH_SIZE_scale']:.4f}, "
+                  f"write {counters['WRITE_SIZE_scale']:.4f} |",
+                  f"| HBM read bytes per launch (scaled) | {f1:,.0f} |",
+                  f"| HBM write bytes per launch (scaled) | {w1:,.0f} |",
+                  f"| algorithmic reads / writes | {rd:,} / {alg - rd:,} |",
+                  f"| measured / algorithmic | reads {f1 / rd:.4f}, writes {w1 / (alg - rd):.4f} |"]
+    with open(os.path.join(out, name + ".md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    with open(os.path.join(out, name + ".json"), "w") as fh:
+        json.dump(data, fh, indent=1)
+    return os.path.join(out, name + ".md")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="long_gqa")
+    ap.add_argument("--mode", default="decode", choices=["decode", "cache_write"])
     ap.add_argument("--out", default="gpurun_out/prof")
     ap.add_argument("--pmc", action="store_true", help="HBM FETCH_SIZE / WRITE_SIZE passes")
     ap.add_argument("--sq", action="store_true", help="instruction-mix / utilisation passes")
@@ -248,10 +321,13 @@ def main():
     a = ap.parse_args()
     out = os.path.abspath(a.out)
     os.makedirs(out, exist_ok=True)
-    trace = kernel_trace(a.config, out, a.steps)
-    counters = pmc(a.config, out) if a.pmc else None
-    sqv = sq(a.config, out) if a.sq else None
-    path = write_summary(a.config, out, trace, counters, sqv)
+    trace = kernel_trace(a.config, out, a.steps, a.mode)
+    counters = pmc(a.config, out, a.mode) if a.pmc else None
+    if a.mode == "cache_write":
+        path = write_cache_summary(a.config, out, trace, counters)
+    else:
+        sqv = sq(a.config, out) if a.sq else None
+        path = write_summary(a.config, out, trace, counters, sqv)
     print(open(path).read(), flush=True)
 
 

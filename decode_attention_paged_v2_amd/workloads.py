@@ -262,3 +262,63 @@ SMALL_SPECS = {
                    lambda g: [2048, 1500, 33, 4096], pool=lambda n: n + 19,
                    k_scale=0.05, v_scale=0.04, seed=2005),
 }
+
+
+# ---- KV-cache write inputs ---------------------------------------------------
+
+@dataclass
+class CacheWriteWorkload:
+    """New tokens to write into a paged cache: key, value [T, kv_h, d] in the
+    workload's query dtype, slot_mapping [T] int64, and the (unwritten) caches."""
+    name: str
+    key: torch.Tensor
+    value: torch.Tensor
+    key_cache: torch.Tensor
+    value_cache: torch.Tensor
+    slot_mapping: torch.Tensor
+    k_scale: float
+    v_scale: float
+    cache_dtype: torch.dtype
+
+    def bytes_moved(self) -> int:
+        """Input bytes read plus cache bytes written (key and value)."""
+        T, kvh, d = self.key.shape
+        return T * kvh * d * 2 * (self.key.element_size() + self.key_cache.element_size())
+
+
+def cache_write_workload(spec: Spec, device="cpu", decode_step: bool = False,
+                         seed: Optional[int] = None) -> CacheWriteWorkload:
+    """The whole context of a workload as one write (the prefill of every
+    sequence: each sequence's tokens in order, through its shuffled block
+    table), or with ``decode_step`` one new token per sequence at position
+    seq_len - 1.  Values N(0,1) in the query dtype; the caches are allocated
+    empty (their prior contents are not part of the write)."""
+    seed = spec.seed if seed is None else seed
+    gen_dev = torch.device(device)
+    g = torch.Generator(device=gen_dev)
+    g.manual_seed(seed + 500)
+    gl = torch.Generator()
+    gl.manual_seed(seed)
+    lens = [int(v) for v in spec.lens(gl)]
+    KVH, D, BS = spec.num_kv_heads, spec.head_size, spec.block_size
+    in_dt, cdt = _DT[spec.q_dtype], _DT[spec.kv_dtype]
+    x = x_pack(cdt)
+    need = [(L + BS - 1) // BS for L in lens]
+    total = sum(need)
+    pool = spec.pool(total) if spec.pool else total
+    perm = torch.randperm(pool, generator=gl)
+    slots, off = [], 0
+    for L, n in zip(lens, need):
+        blocks = perm[off:off + n]
+        off += n
+        t = torch.arange(L - 1, L) if decode_step else torch.arange(L)
+        if L > 0:
+            slots.append(blocks[t // BS].long() * BS + t % BS)
+    slot_mapping = (torch.cat(slots) if slots else torch.empty(0, dtype=torch.int64)).to(gen_dev)
+    T = slot_mapping.numel()
+    key = torch.randn((T, KVH, D), generator=g, dtype=torch.float32, device=gen_dev).to(in_dt)
+    value = torch.randn((T, KVH, D), generator=g, dtype=torch.float32, device=gen_dev).to(in_dt)
+    key_cache = torch.empty((pool, KVH, D // x, BS, x), dtype=cdt, device=gen_dev)
+    value_cache = torch.empty((pool, KVH, D, BS), dtype=cdt, device=gen_dev)
+    return CacheWriteWorkload(spec.name + ("_decode_step" if decode_step else "_prefill"), key, value,
+                              key_cache, value_cache, slot_mapping, spec.k_scale, spec.v_scale, cdt)

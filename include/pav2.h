@@ -203,6 +203,41 @@ int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype
                    pav2_dtype_t compute_dtype, pav2_stream_t stream);
 
 /*
+ * KV-cache write (page "paged_attn.py", write_to_paged_cache, which passes
+ * key, value, key_cache, value_cache, slot_mapping, kv_cache_dtype, k_scale
+ * and v_scale to reshape_and_cache): stores the keys and values of
+ * num_tokens new tokens into the paged caches that the decode entry points
+ * read.  Token t goes to slot s = slot_mapping[t], i.e. block s / block_size,
+ * offset s % block_size:
+ *
+ *   key_cache  [s / bs, g, i / x, s % bs, i % x] = enc(key  [t, g, i] / k_scale)
+ *   value_cache[s / bs, g, i,     s % bs]        = enc(value[t, g, i] / v_scale)
+ *
+ * The inverse of the decode gather, which multiplies by k_scale / v_scale.
+ * The quotient is an IEEE float32 division; enc rounds it to kv_cache_dtype
+ * to nearest, ties to even (FP8_E4M3 saturates at +-448 first; NaN stays
+ * NaN).  With unit scales and kv_cache_dtype == input_dtype the write copies
+ * the input bits.
+ *
+ *   key, value    [num_tokens, num_kv_heads, head_size] input_dtype (F32, F16, BF16)
+ *   key_cache     [num_blocks, num_kv_heads, head_size/x, block_size, x] kv_cache_dtype
+ *   value_cache   [num_blocks, num_kv_heads, head_size, block_size]      kv_cache_dtype
+ *   slot_mapping  [num_tokens] int64
+ *
+ * kv_cache_dtype is input_dtype or FP8_E4M3.  A slot < 0 ("no slot", e.g. a
+ * padding token) or >= num_blocks * block_size writes nothing.  Two tokens
+ * with the same slot leave either one's data there.  head_size and
+ * block_size as for the decode entry points; k_scale and v_scale finite and
+ * > 0.  num_tokens == 0 launches nothing.  All pointers are device memory
+ * owned by the caller; asynchronous on `stream`; allocates nothing.
+ */
+int pav2_reshape_and_cache(
+    const void *key, const void *value, void *key_cache, void *value_cache,
+    const int64_t *slot_mapping, pav2_dtype_t kv_cache_dtype, float k_scale, float v_scale,
+    int num_tokens, int num_kv_heads, int head_size, int block_size, int num_blocks,
+    pav2_dtype_t input_dtype, pav2_stream_t stream);
+
+/*
  * Debug validator for the device data the decode entry points take on trust:
  * every seq_lens[s] in [0, max_blocks_per_seq * block_size], and every
  * block_tables[s][j] with j < ceil(seq_lens[s] / block_size) in

@@ -211,3 +211,45 @@ def test_python_binding_has_no_cpu_path():
                                 q, torch.zeros(2, 4, 16, 16, 4), torch.zeros(2, 4, 64, 16), 4, 0.125,
                                 torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32),
                                 16, 1)
+
+
+def test_reshape_and_cache_validation():
+    lib = pav2.load()
+    v = ctypes.c_void_p(16)
+
+    def call(**over):
+        a = dict(key=v, value=v, key_cache=v, value_cache=v, slot_mapping=v, kv_cache_dtype=B.BF16,
+                 k_scale=1.0, v_scale=1.0, num_tokens=4, num_kv_heads=4, head_size=256, block_size=16,
+                 num_blocks=100, input_dtype=B.BF16, stream=None)
+        a.update(over)
+        return lib.pav2_reshape_and_cache(*a.values())
+    assert call(num_tokens=-1) == -1
+    assert call(num_kv_heads=0) == -1
+    assert call(num_blocks=0) == -1
+    assert call(input_dtype=B.FP8_E4M3, kv_cache_dtype=B.FP8_E4M3) == -1
+    assert call(kv_cache_dtype=B.F16) == -2                       # neither the input dtype nor fp8
+    assert call(head_size=100) == -2
+    assert call(head_size=120, kv_cache_dtype=B.FP8_E4M3) == -2   # 120 % 16 != 0
+    assert call(block_size=24) == -2
+    assert call(block_size=4) == -2
+    assert call(k_scale=0.0) == -1
+    assert call(v_scale=float("inf")) == -1
+    assert call(k_scale=float("nan")) == -1
+    assert call(slot_mapping=None) == -1
+    assert "NULL" in pav2.last_error()
+    # nothing to write: succeeds without a launch, even with null pointers
+    assert call(num_tokens=0, key=None, value=None, key_cache=None, value_cache=None, slot_mapping=None) == 0
+
+
+def test_reshape_and_cache_binding_checks_shapes():
+    import torch
+    k = torch.zeros(3, 2, 64)
+    with pytest.raises(ValueError, match="int64"):
+        pav2.reshape_and_cache(k, k, torch.zeros(4, 2, 16, 16, 4), torch.zeros(4, 2, 64, 16),
+                               torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="cache shapes"):
+        pav2.reshape_and_cache(k, k, torch.zeros(4, 2, 16, 16, 4), torch.zeros(4, 3, 64, 16),
+                               torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(ValueError, match="device tensor"):
+        pav2.reshape_and_cache(k, k, torch.zeros(4, 2, 16, 16, 4), torch.zeros(4, 2, 64, 16),
+                               torch.zeros(3, dtype=torch.int64))
