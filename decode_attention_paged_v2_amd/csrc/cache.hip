@@ -13,26 +13,37 @@
 // scales and a cache of the input's dtype the write is a plain copy.  Slots
 // < 0, or past the pool, write nothing.
 //
-// One workgroup per (16 consecutive tokens, kv head).  Keys: a lane converts
-// one 16-byte cache vector (x elements of one token) and stores it; lanes are
-// token-fastest, so tokens with consecutive slots give contiguous stores, and
-// the four vectors a wavefront takes from one token are 64 contiguous input
-// bytes.  Values: a token's head-dim row must be scattered over d cache rows
-// of block_size elements, so the tile is transposed through LDS; each lane
-// then stores 8 tokens of one head-dim row as one vector when their slots are
-// 8 consecutive, 8-aligned positions (always within one block, as block sizes
-// are powers of two >= 8), else element by element.
+// One workgroup per (tile of consecutive tokens, kv head): 16 tokens, or 32
+// for one-byte caches so that a prefill tile fills whole 32-byte value rows
+// of a 32-token block (a half-written row would leave each 64-byte line to
+// two workgroups).  The tile moves through LDS in both directions:
+//
+// * loads: lanes take consecutive 16-byte vectors of the tile's token rows
+//   (a token's row for one kv head is d contiguous elements), so every
+//   wavefront reads whole lines; each vector is converted to the cache dtype
+//   and written to LDS -- keys in cache order as 16-byte cache vectors
+//   [chunk][token], values as converted token rows [token][head dim] (rows
+//   padded by 16 bytes, so neither the row writes nor the column reads below
+//   conflict in LDS banks);
+// * stores: keys token-fastest (tokens with consecutive slots give
+//   block_size * 16 contiguous bytes per chunk); values as 8 tokens of one
+//   head-dim row per lane (gathered from the 8 token rows in LDS), one vector
+//   store when their slots are 8
+//   consecutive, 8-aligned positions (always within one block, as block
+//   sizes are powers of two >= 8), else element by element.
 #include "pav2_internal.h"
 
 namespace pav2 {
 namespace {
 
-constexpr int kTileTokens = 16;
 constexpr int kCacheThreads = 256;
 constexpr int kMaxHead = 256;
 
 template <int DT>
 constexpr int esize() { return DT == F32 ? 4 : (DT == FP8 ? 1 : 2); }
+
+template <int CDT>
+constexpr int tile_tokens() { return esize<CDT>() == 1 ? 32 : 16; }
 
 // Element e of a run of 32-bit words holding elements of dtype DT, as float.
 template <int DT>
@@ -82,22 +93,16 @@ __device__ __forceinline__ void encode(const float (&f)[N], uint32_t (&w)[N * es
     }
 }
 
-// N input elements at `src` (16-byte aligned) -> N cache elements in words.
-template <int IDT, int CDT, bool SCALED, int N>
-__device__ __forceinline__ void convert(const uint8_t *src, float scale, uint32_t (&out)[N * esize<CDT>() / 4]) {
-    constexpr int IW = N * esize<IDT>() / 4;   // input words
-    uint32_t in[IW];
-#pragma unroll
-    for (int k = 0; k < IW / 4; ++k) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src) + k);
-        in[4 * k + 0] = v[0];
-        in[4 * k + 1] = v[1];
-        in[4 * k + 2] = v[2];
-        in[4 * k + 3] = v[3];
-    }
+// One 16-byte input vector (16 / sizeof(input) elements) -> the same
+// elements in the cache dtype, packed in words.
+template <int IDT, int CDT, bool SCALED>
+__device__ __forceinline__ void convert16(const u32x4 v, float scale,
+                                          uint32_t (&out)[(16 / esize<IDT>()) * esize<CDT>() / 4]) {
+    constexpr int N = 16 / esize<IDT>();
+    const uint32_t in[4] = {v[0], v[1], v[2], v[3]};
     if constexpr (IDT == CDT && !SCALED) {
 #pragma unroll
-        for (int k = 0; k < IW; ++k) out[k] = in[k];   // x / 1 rounds to x: copy the bits
+        for (int k = 0; k < 4; ++k) out[k] = in[k];   // x / 1 rounds to x: copy the bits
     } else {
         float f[N];
 #pragma unroll
@@ -110,7 +115,7 @@ __device__ __forceinline__ void convert(const uint8_t *src, float scale, uint32_
 }
 
 template <int NW>
-__device__ __forceinline__ void store_words(uint8_t *dst, const uint32_t (&w)[NW]) {
+__device__ __forceinline__ void store_words(uint8_t *dst, const uint32_t *w) {
     if constexpr (NW == 2) {
         __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2 *>(dst));
     } else {
@@ -121,73 +126,75 @@ __device__ __forceinline__ void store_words(uint8_t *dst, const uint32_t (&w)[NW
     }
 }
 
-template <int IDT, int CDT, bool SCALED>
+template <int IDT, int CDT, int D, bool SCALED>
 __global__ void __launch_bounds__(kCacheThreads) cache_write_kernel(const CacheParams P) {
     constexpr int IB = esize<IDT>();
     constexpr int CB = esize<CDT>();
-    constexpr int X = 16 / CB;            // elements per 16-byte key vector
-    constexpr int RS = kTileTokens * CB + 16;   // LDS row stride (bytes) of the transposed values
-    __shared__ __align__(16) uint8_t s_v[kMaxHead * RS];
-    __shared__ int64_t s_slot[kTileTokens];
+    constexpr int X = 16 / CB;            // elements per 16-byte cache vector (keys)
+    constexpr int EV = 16 / IB;           // elements per 16-byte input vector
+    constexpr int NV = D / EV;            // input vectors per token row
+    constexpr int NC = D / X;             // cache vectors (key chunks) per token
+    constexpr int TT = tile_tokens<CDT>();
+    constexpr int NG = TT / 8;            // 8-token value groups per tile
+    constexpr int SK = TT * 16 + 16;      // LDS bytes per key chunk row (padded)
+    constexpr int RV = D * CB + 16;       // LDS bytes per converted value token row (padded)
+    __shared__ __align__(16) uint8_t s_k[NC * SK];
+    __shared__ __align__(16) uint8_t s_v[TT * RV];
+    __shared__ int64_t s_slot[TT];
 
     const int tid = threadIdx.x;
-    const int t = tid & (kTileTokens - 1);
-    const int j = tid >> 4;
     const int g = blockIdx.y;
-    const int64_t t0 = (int64_t)blockIdx.x * kTileTokens;
-    const int D = P.head_size;
+    const int64_t t0 = (int64_t)blockIdx.x * TT;
     const int bs_log2 = P.bs_log2;
     const int64_t bs_mask = (1 << bs_log2) - 1;
     const int64_t row_in = (int64_t)P.num_kv_heads * D * IB;   // input bytes per token
+    const int ntok = (int)min((int64_t)TT, P.num_tokens - t0);
 
-    if (tid < kTileTokens) {
+    if (tid < TT) {
         int64_t sl = -1;
-        if (t0 + tid < P.num_tokens) sl = P.slot_mapping[t0 + tid];
+        if (tid < ntok) sl = P.slot_mapping[t0 + tid];
         s_slot[tid] = (sl >= 0 && sl < P.num_slots) ? sl : -1;
     }
 
-    // values: 8 head-dim elements of token t per step, transposed into LDS
-    const bool tok_ok = t0 + t < P.num_tokens;
-    const uint8_t *vin = P.value + (t0 + t) * row_in + (int64_t)g * D * IB;
-    for (int c = j; c < D / 8; c += kCacheThreads / kTileTokens) {
-        uint32_t w[8 * CB / 4 > 0 ? 8 * CB / 4 : 1];
-        if (tok_ok) {
-            convert<IDT, CDT, SCALED, 8>(vin + c * 8 * IB, P.v_scale, w);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8 * CB / 4; ++k) w[k] = 0u;
-        }
-        const uint8_t *wb = reinterpret_cast<const uint8_t *>(w);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            uint8_t *dst = s_v + (8 * c + k) * RS + t * CB;
-            if constexpr (CB == 4) *reinterpret_cast<uint32_t *>(dst) = w[k];
-            else if constexpr (CB == 2) *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
-            else *dst = wb[k];
-        }
+    // loads: keys (vectors [0, TT * NV)), then values; consecutive lanes take
+    // consecutive vectors of a token row
+    const uint8_t *kin = P.key + t0 * row_in + (int64_t)g * D * IB;
+    const uint8_t *vin = P.value + t0 * row_in + (int64_t)g * D * IB;
+    constexpr int OW = EV * CB / 4;       // cache words per input vector
+    for (int v = tid; v < 2 * TT * NV; v += kCacheThreads) {
+        const bool is_v = v >= TT * NV;
+        const int u = is_v ? v - TT * NV : v;
+        const int t = u / NV, k = u - t * NV;
+        if (t >= ntok) continue;
+        const uint8_t *src = (is_v ? vin : kin) + t * row_in + k * 16;
+        const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+        uint32_t w[OW > 0 ? OW : 1];
+        convert16<IDT, CDT, SCALED>(raw, is_v ? P.v_scale : P.k_scale, w);
+        // keys: elements k*EV .. k*EV+EV-1 lie in key chunk k / (X/EV);
+        // values: the same bytes of the token's converted row
+        uint8_t *dst = is_v ? s_v + t * RV + k * EV * CB
+                            : s_k + (k / (X / EV)) * SK + t * 16 + (k % (X / EV)) * EV * CB;
+        if constexpr (OW == 4) *reinterpret_cast<u32x4 *>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+        else if constexpr (OW == 2) *reinterpret_cast<u32x2 *>(dst) = u32x2{w[0], w[1]};
+        else *reinterpret_cast<uint32_t *>(dst) = w[0];
     }
     __syncthreads();
 
     const int64_t head_off = (int64_t)g * P.head_stride;
 
-    // keys: one 16-byte cache vector (x elements) per lane and step
-    {
+    // keys: one 16-byte cache vector per lane, tokens fastest
+    for (int idx = tid; idx < NC * TT; idx += kCacheThreads) {
+        const int t = idx % TT, c = idx / TT;
         const int64_t sl = s_slot[t];
-        if (sl >= 0) {
-            const uint8_t *kin = P.key + (t0 + t) * row_in + (int64_t)g * D * IB;
-            uint8_t *kout = P.key_cache + (sl >> bs_log2) * P.blk_stride + head_off + (sl & bs_mask) * 16;
-            const int nc = D / X;
-            for (int c = j; c < nc; c += kCacheThreads / kTileTokens) {
-                uint32_t w[4];
-                convert<IDT, CDT, SCALED, X>(kin + c * X * IB, P.k_scale, w);
-                store_words<4>(kout + ((int64_t)c << (bs_log2 + 4)), w);
-            }
-        }
+        if (sl < 0) continue;
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(s_k + c * SK + t * 16);
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(P.key_cache + (sl >> bs_log2) * P.blk_stride +
+                                                                  head_off + (((int64_t)c << bs_log2) + (sl & bs_mask)) * 16));
     }
 
-    // values: 8 tokens of one head-dim row per lane and step
+    // values: 8 tokens of one head-dim row per lane
     {
-        const int h = tid & 1;
+        const int h = tid % NG;
         int64_t sl[8];
         bool run = true;
 #pragma unroll
@@ -197,37 +204,63 @@ __global__ void __launch_bounds__(kCacheThreads) cache_write_kernel(const CacheP
         }
         run = run && (sl[0] & 7) == 0;
         uint8_t *vbase = P.value_cache + head_off;
-        for (int i = tid >> 1; i < D; i += kCacheThreads / 2) {
-            const uint8_t *src = s_v + i * RS + 8 * h * CB;
-            if (run) {
-                uint32_t w[8 * CB / 4];
+        for (int i = tid / NG; i < D; i += kCacheThreads / NG) {
+            // element i of tokens 8h .. 8h+7, packed in words
+            uint32_t w[8 * CB / 4];
 #pragma unroll
-                for (int k = 0; k < 8 * CB / 4; ++k) w[k] = reinterpret_cast<const uint32_t *>(src)[k];
+            for (int k = 0; k < 8 * CB / 4; ++k) w[k] = 0u;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint8_t *src = s_v + (8 * h + k) * RV + i * CB;
+                if constexpr (CB == 4) w[k] = *reinterpret_cast<const uint32_t *>(src);
+                else if constexpr (CB == 2) w[k >> 1] |= (uint32_t)*reinterpret_cast<const uint16_t *>(src) << (16 * (k & 1));
+                else w[k >> 2] |= (uint32_t)*src << (8 * (k & 3));
+            }
+            if (run) {
                 store_words<8 * CB / 4>(vbase + (sl[0] >> bs_log2) * P.blk_stride +
                                             (((int64_t)i << bs_log2) + (sl[0] & bs_mask)) * CB, w);
             } else {
+                const uint8_t *wb = reinterpret_cast<const uint8_t *>(w);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     if (sl[k] < 0) continue;
                     uint8_t *dst = vbase + (sl[k] >> bs_log2) * P.blk_stride +
                                    (((int64_t)i << bs_log2) + (sl[k] & bs_mask)) * CB;
-                    if constexpr (CB == 4) *reinterpret_cast<uint32_t *>(dst) = reinterpret_cast<const uint32_t *>(src)[k];
-                    else if constexpr (CB == 2) *reinterpret_cast<uint16_t *>(dst) = reinterpret_cast<const uint16_t *>(src)[k];
-                    else *dst = src[k];
+                    if constexpr (CB == 4) *reinterpret_cast<uint32_t *>(dst) = w[k];
+                    else if constexpr (CB == 2) *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+                    else *dst = wb[k];
                 }
             }
         }
     }
 }
 
+template <int IDT, int CDT, int D>
+hipError_t launch_d(const CacheParams &p, bool scaled, hipStream_t stream) {
+    constexpr int TT = tile_tokens<CDT>();
+    const dim3 grid((unsigned)((p.num_tokens + TT - 1) / TT), (unsigned)p.num_kv_heads);
+    if (scaled)
+        hipLaunchKernelGGL((cache_write_kernel<IDT, CDT, D, true>), grid, dim3(kCacheThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((cache_write_kernel<IDT, CDT, D, false>), grid, dim3(kCacheThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <int IDT, int CDT>
 hipError_t launch_scaled(const CacheParams &p, bool scaled, hipStream_t stream) {
-    const dim3 grid((unsigned)((p.num_tokens + kTileTokens - 1) / kTileTokens), (unsigned)p.num_kv_heads);
-    if (scaled)
-        hipLaunchKernelGGL((cache_write_kernel<IDT, CDT, true>), grid, dim3(kCacheThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((cache_write_kernel<IDT, CDT, false>), grid, dim3(kCacheThreads), 0, stream, p);
-    return hipGetLastError();
+    switch (p.head_size) {
+    case 64: return launch_d<IDT, CDT, 64>(p, scaled, stream);
+    case 80: return launch_d<IDT, CDT, 80>(p, scaled, stream);
+    case 96: return launch_d<IDT, CDT, 96>(p, scaled, stream);
+    case 112: return launch_d<IDT, CDT, 112>(p, scaled, stream);
+    case 128: return launch_d<IDT, CDT, 128>(p, scaled, stream);
+    case 192: return launch_d<IDT, CDT, 192>(p, scaled, stream);
+    case 256: return launch_d<IDT, CDT, 256>(p, scaled, stream);
+    case 120:
+        if constexpr (CDT != FP8) return launch_d<IDT, CDT, 120>(p, scaled, stream);
+        else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int IDT>

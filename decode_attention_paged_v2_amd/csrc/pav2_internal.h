@@ -119,20 +119,6 @@ constexpr int kMaxCompactSeqs = 8192;
 #define PAV2_PHASE1_COMPACT_ROUNDS 8
 #endif
 constexpr int kPhase1CompactRounds = PAV2_PHASE1_COMPACT_ROUNDS;
-// Cap on the resident workgroups per CU the compact grid is sized for (0: the
-// occupancy the kernel's resources allow).
-#ifndef PAV2_PHASE1_MAX_PER_CU
-#define PAV2_PHASE1_MAX_PER_CU 0
-#endif
-constexpr int kPhase1MaxPerCU = PAV2_PHASE1_MAX_PER_CU;
-// Order of the compact list: 0 = (sequence, partition, kv head, head group),
-// consecutive items are the kv heads of one partition; 1 = (sequence, kv
-// head, head group, partition), consecutive items are consecutive partitions
-// of one (sequence, kv head, head group).
-#ifndef PAV2_PHASE1_ITEM_ORDER
-#define PAV2_PHASE1_ITEM_ORDER 0
-#endif
-constexpr int kPhase1ItemOrder = PAV2_PHASE1_ITEM_ORDER;
 
 inline bool phase1_compact(int num_seqs) {
     if (PAV2_PHASE1_SCHEDULE == 0) return false;
