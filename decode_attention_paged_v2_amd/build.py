@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpav2.so")
 SOURCES = ["api.hip", "phase1.hip", "phase2.hip", "check.hip", "cache.hip"]
-HEADERS = [os.path.join(CSRC, "pav2_internal.h"), os.path.join(ROOT, "include", "pav2.h")]
+HEADERS = [os.path.join(CSRC, "pav2_internal.h"), os.path.join(CSRC, "cache.h"), os.path.join(ROOT, "include", "pav2.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -8,6 +8,7 @@
 
 #include "../../include/pav2.h"
 #include "pav2_internal.h"
+#include "cache.h"
 
 namespace {
 
@@ -408,6 +409,10 @@ int pav2_reshape_and_cache(const void *key, const void *value, void *key_cache, 
     p.blk_stride = p.head_stride * num_kv_heads;
     p.k_scale = k_scale;
     p.v_scale = v_scale;
+    p.k_rcp = 1.0f / k_scale;
+    p.v_rcp = 1.0f / v_scale;
+    const auto normal_rcp = [](float sc) { return sc >= 0x1p-100f && sc <= 0x1p100f; };
+    p.fast_div = normal_rcp(k_scale) && normal_rcp(v_scale) ? 1 : 0;
     return launch_status(pav2::launch_cache_write(p, (int)input_dtype, (int)kv_cache_dtype,
                                                   static_cast<hipStream_t>(stream)),
                          "reshape_and_cache");

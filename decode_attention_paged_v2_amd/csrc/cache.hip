@@ -8,7 +8,8 @@
 //   value_cache[blk, g, i,     off]        = enc(value[t, g, i] / v_scale)
 //
 // with x = 16 / element size of the cache dtype.  The quotient is an IEEE
-// float32 division; enc rounds to the cache dtype to nearest, ties to even
+// float32 division (computed exactly as such, see quotient()); enc rounds to
+// the cache dtype to nearest, ties to even
 // (e4m3 after saturating to +-448, so no value overflows to NaN).  With unit
 // scales and a cache of the input's dtype the write is a plain copy.  Slots
 // < 0, or past the pool, write nothing.
@@ -31,7 +32,7 @@
 //   store when their slots are 8
 //   consecutive, 8-aligned positions (always within one block, as block
 //   sizes are powers of two >= 8), else element by element.
-#include "pav2_internal.h"
+#include "cache.h"
 
 namespace pav2 {
 namespace {
@@ -93,10 +94,24 @@ __device__ __forceinline__ void encode(const float (&f)[N], uint32_t (&w)[N * es
     }
 }
 
+// a / b rounded to nearest (IEEE float32 division), given y = RN(1 / b).
+// Fast path (Markstein's correction): q = RN(a * y) is within one ulp of
+// a / b, the residual a - b * q is exact in one FMA, and RN(q + r * y) is the
+// correctly rounded quotient -- valid while a, q and the residual stay well
+// inside the normal range (checked per element) and y is normal (checked on
+// the host, `fast`).  Everything else takes the division itself.
+__device__ __forceinline__ float quotient(float a, float b, float y, bool fast) {
+    const float q = a * y;
+    const float aq = fabsf(q), aa = fabsf(a);
+    if (fast && aq >= 0x1p-100f && aq <= 0x1p100f && aa >= 0x1p-96f && aa <= 0x1p100f)
+        return fmaf(fmaf(-q, b, a), y, q);
+    return a / b;
+}
+
 // One 16-byte input vector (16 / sizeof(input) elements) -> the same
 // elements in the cache dtype, packed in words.
 template <int IDT, int CDT, bool SCALED>
-__device__ __forceinline__ void convert16(const u32x4 v, float scale,
+__device__ __forceinline__ void convert16(const u32x4 v, float scale, float rcp, bool fast,
                                           uint32_t (&out)[(16 / esize<IDT>()) * esize<CDT>() / 4]) {
     constexpr int N = 16 / esize<IDT>();
     const uint32_t in[4] = {v[0], v[1], v[2], v[3]};
@@ -108,7 +123,7 @@ __device__ __forceinline__ void convert16(const u32x4 v, float scale,
 #pragma unroll
         for (int e = 0; e < N; ++e) {
             f[e] = widen<IDT>(in, e);
-            if constexpr (SCALED) f[e] = f[e] / scale;
+            if constexpr (SCALED) f[e] = quotient(f[e], scale, rcp, fast);
         }
         encode<CDT, N>(f, out);
     }
@@ -169,7 +184,8 @@ __global__ void __launch_bounds__(kCacheThreads) cache_write_kernel(const CacheP
         const uint8_t *src = (is_v ? vin : kin) + t * row_in + k * 16;
         const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
         uint32_t w[OW > 0 ? OW : 1];
-        convert16<IDT, CDT, SCALED>(raw, is_v ? P.v_scale : P.k_scale, w);
+        convert16<IDT, CDT, SCALED>(raw, is_v ? P.v_scale : P.k_scale, is_v ? P.v_rcp : P.k_rcp,
+                                    P.fast_div != 0, w);
         // keys: elements k*EV .. k*EV+EV-1 lie in key chunk k / (X/EV);
         // values: the same bytes of the token's converted row
         uint8_t *dst = is_v ? s_v + t * RV + k * EV * CB

@@ -65,20 +65,6 @@ struct Phase2Params {
     int num_seqs, num_heads, max_num_partitions;
 };
 
-struct CacheParams {
-    const uint8_t *key;            // [T, KVH, D] input dtype
-    const uint8_t *value;          // [T, KVH, D]
-    uint8_t *key_cache;            // [NB, KVH, D/x, BS, x] cache dtype
-    uint8_t *value_cache;          // [NB, KVH, D, BS]
-    const int64_t *slot_mapping;   // [T]
-    int num_tokens, num_kv_heads, head_size;
-    int bs_log2;                   // log2(block_size)
-    int64_t num_slots;             // num_blocks * block_size
-    int64_t blk_stride;            // bytes per physical block (all kv heads)
-    int64_t head_stride;           // bytes per (block, kv head)
-    float k_scale, v_scale;        // the write divides by these
-};
-
 // Host-side launchers (one per translation unit that defines the kernels).
 // Return hipSuccess, or hipErrorInvalidValue for an unsupported combination.
 hipError_t launch_phase1(const Phase1Params &p, int qdt, int kvdt, int head_size,
@@ -87,7 +73,6 @@ hipError_t launch_phase2(const Phase2Params &p, int odt, int head_size, int thre
                          int lds_bytes, hipStream_t stream);
 hipError_t launch_decode_kv(const void *src, float *dst, int64_t n, int dtype, int via,
                             hipStream_t stream);
-hipError_t launch_cache_write(const CacheParams &p, int input_dtype, int cache_dtype, hipStream_t stream);
 hipError_t launch_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
                                int max_blocks_per_seq, int block_size, int num_blocks, long long *report,
                                hipStream_t stream);

@@ -38,7 +38,7 @@ ROOT = os.path.dirname(HERE)
 BENCH = os.path.join(ROOT, "bench.py")
 KERNEL_SOURCES = {
     "decode": [os.path.join(HERE, "csrc", f) for f in ("phase1.hip", "phase2.hip", "pav2_internal.h")],
-    "cache_write": [os.path.join(HERE, "csrc", f) for f in ("cache.hip", "pav2_internal.h")],
+    "cache_write": [os.path.join(HERE, "csrc", f) for f in ("cache.hip", "cache.h", "pav2_internal.h")],
 }
 
 

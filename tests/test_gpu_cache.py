@@ -275,3 +275,54 @@ def test_write_full_size_sampled(config):
     ii = idx.to(DEV)
     assert torch.equal(kg[ii].cpu().view(torch.uint8), want_k.view(torch.uint8)), es
     assert torch.equal(vg[ii].cpu().view(torch.uint8), want_v.view(torch.uint8))
+
+
+@pytest.mark.parametrize("cache_dt", ["fp8_e4m3", "bf16", "f16"])
+@pytest.mark.parametrize("scale", [0.05, 0.04, 0.37, 3.1, 2.0 ** -90, 2.0 ** 90])
+def test_write_scaled_quotients_at_rounding_edges(cache_dt, scale):
+    """Inputs whose quotient by the scale lies within a float32 ulp of a rounding
+    midpoint of the cache dtype (and of representable values), plus inputs
+    around the magnitudes where the kernel switches between its FMA-corrected
+    quotient and the division itself: every byte must match the oracle's IEEE
+    float32 division followed by round-to-nearest-even."""
+    print(f"case quotient edges {cache_dt} scale={scale}", flush=True)
+    gen = torch.Generator().manual_seed(31)
+    if cache_dt == "fp8_e4m3":
+        codes = torch.arange(0, 0x7E, dtype=torch.uint8)
+        lo = codes.view(torch.float8_e4m3fn).double()
+        hi = (codes + 1).view(torch.float8_e4m3fn).double()
+    else:
+        dt = _TD[cache_dt]
+        codes = torch.randint(0, 0x7B00 if cache_dt == "f16" else 0x7F00, (4000,), generator=gen, dtype=torch.int32)
+        lo = codes.to(torch.int16).view(dt).double()
+        hi = (codes + 1).to(torch.int16).view(dt).double()
+    targets = torch.cat([(lo + hi) / 2, lo])
+    x = (targets * scale).float()                               # RN32(target * s)
+    up = torch.nextafter(x, torch.full_like(x, float("inf")))
+    dn = torch.nextafter(x, torch.full_like(x, float("-inf")))
+    special = torch.tensor([2.0 ** -97, 2.0 ** -96, 2.0 ** -95, 1.5 * 2.0 ** -96, 2.0 ** -126, 1e-40, 0.0,
+                            2.0 ** 99, 2.0 ** 100, 2.0 ** 101, 3e38], dtype=torch.float64)
+    vals = torch.cat([x, up, dn, special.float(), (special * scale).float()])
+    vals = torch.cat([vals, -vals])
+    vals = vals[torch.isfinite(vals)]
+    d, kvh = 128, 1
+    T = (vals.numel() + d - 1) // d
+    flat = torch.zeros(T * d)
+    flat[:vals.numel()] = vals
+    key = flat.view(T, kvh, d)
+    value = key.flip(0).contiguous()
+    slots = torch.arange(T, dtype=torch.int64)
+    nb = (T + 15) // 16
+    kc, vc = poisoned(nb, kvh, d, 16, cache_dt)
+    gk, gv = kc.to(DEV), vc.to(DEV)
+    # fp8 caches take the float32 values; a 16-bit cache takes inputs of its
+    # own dtype (the values rounded to it)
+    if cache_dt != "fp8_e4m3":
+        key, value = key.to(_TD[cache_dt]), value.to(_TD[cache_dt])
+    rk, rv = oracle.reshape_and_cache(key, value, kc, vc, slots, block_size=16, cache_dtype=_CODE[cache_dt],
+                                      k_scale=scale, v_scale=scale)
+    pav2.reshape_and_cache(key.to(DEV), value.to(DEV), gk, gv, slots.to(DEV),
+                           "fp8_e4m3" if cache_dt == "fp8_e4m3" else "auto", scale, scale)
+    torch.cuda.synchronize()
+    assert_same_bytes(gk.cpu(), rk)
+    assert_same_bytes(gv.cpu(), rv)
