@@ -104,6 +104,13 @@ constexpr int kMaxCompactSeqs = 8192;
 #define PAV2_PHASE1_COMPACT_ROUNDS 8
 #endif
 constexpr int kPhase1CompactRounds = PAV2_PHASE1_COMPACT_ROUNDS;
+// 1: the compact grid's workgroups on one XCD (blockIdx % 8) take one
+// contiguous block of the item list, so each XCD's L2 holds the output rows
+// and block-table entries of neighbouring items.
+#ifndef PAV2_PHASE1_XCD_RANGES
+#define PAV2_PHASE1_XCD_RANGES 1
+#endif
+constexpr int kPhase1XcdRanges = PAV2_PHASE1_XCD_RANGES;
 
 inline bool phase1_compact(int num_seqs) {
     if (PAV2_PHASE1_SCHEDULE == 0) return false;

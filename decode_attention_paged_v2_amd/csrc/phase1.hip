@@ -191,7 +191,8 @@ phase1_kernel(const Phase1Params P) {
     // slot per workgroup, consecutive slots on one XCD (blockIdx.x % 8).
     // Compact schedule: the workgroup computes the exclusive prefix of the
     // sequences' partition counts from seq_lens in LDS and takes a contiguous
-    // range of the list of used (seq, partition, kv head, head group) items.
+    // range of the list of used (seq, partition, kv head, head group) items;
+    // the workgroups of one XCD (blockIdx % 8) take one contiguous block of it.
     // Single pass: the items are the partitions of one (seq, kv head, head
     // group), blockIdx.x, taken in order.
     int item, item_end;
@@ -237,8 +238,12 @@ phase1_kernel(const Phase1Params P) {
         total = __builtin_amdgcn_readfirstlane(total);   // wave-uniform: keep the item loop scalar
         __syncthreads();
         const int64_t n_items = (int64_t)total * KVH * HG;
-        item = (int)(n_items * blockIdx.x / gridDim.x);            // balanced contiguous ranges
-        item_end = (int)(n_items * (blockIdx.x + 1) / gridDim.x);
+        // balanced contiguous ranges; the XCD-blocked numbering is a
+        // permutation of the workgroups when the grid is a multiple of 8
+        const bool xcd = kPhase1XcdRanges && (gridDim.x & 7) == 0;
+        const int b = xcd ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
+        item = (int)(n_items * b / gridDim.x);
+        item_end = (int)(n_items * (b + 1) / gridDim.x);
     } else {
         const int nblk = gridDim.x;
         item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
