@@ -322,3 +322,85 @@ def cache_write_workload(spec: Spec, device="cpu", decode_step: bool = False,
     value_cache = torch.empty((pool, KVH, D, BS), dtype=cdt, device=gen_dev)
     return CacheWriteWorkload(spec.name + ("_decode_step" if decode_step else "_prefill"), key, value,
                               key_cache, value_cache, slot_mapping, spec.k_scale, spec.v_scale, cdt)
+
+
+# ---- paged prefix attention (chunked prefill) inputs -------------------------
+
+@dataclass
+class PrefixWorkload:
+    """Chunks of new query tokens over sequences whose first context_lens[i]
+    tokens are already in the paged cache.  query [T, H, d], key / value
+    [T, kv_h, d] (the chunks' own keys and values), block tables covering
+    context + chunk, and slot_mapping [T] (int64): where each chunk token's
+    key / value go in the cache.  Chunk slots in the cache hold NaN until
+    written."""
+    query: torch.Tensor
+    key: torch.Tensor
+    value: torch.Tensor
+    key_cache: torch.Tensor
+    value_cache: torch.Tensor
+    block_tables: torch.Tensor
+    query_start_loc: torch.Tensor
+    context_lens: torch.Tensor
+    slot_mapping: torch.Tensor
+    num_kv_heads: int
+    block_size: int
+    ctx_host: list
+    qlen_host: list
+
+    @property
+    def max_query_len(self):
+        return max(self.qlen_host) if self.qlen_host else 0
+
+    def to(self, device) -> "PrefixWorkload":
+        mv = lambda t: t.to(device)
+        return PrefixWorkload(mv(self.query), mv(self.key), mv(self.value), mv(self.key_cache),
+                              mv(self.value_cache), mv(self.block_tables), mv(self.query_start_loc),
+                              mv(self.context_lens), mv(self.slot_mapping), self.num_kv_heads,
+                              self.block_size, list(self.ctx_host), list(self.qlen_host))
+
+
+def prefix_workload(ctx_lens, q_lens, num_heads, num_kv_heads, head_size, block_size, dtype="bf16",
+                    seed=0, device="cpu", extra_blocks=3) -> PrefixWorkload:
+    """Seeded inputs: N(0,1) values in `dtype`, shuffled disjoint block tables."""
+    dt = _DT[dtype]
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(seed)
+    gl = torch.Generator()
+    gl.manual_seed(seed)
+    S, H, KVH, D, BS = len(ctx_lens), num_heads, num_kv_heads, head_size, block_size
+    x = x_pack(dt)
+    need = [(c + q + BS - 1) // BS for c, q in zip(ctx_lens, q_lens)]
+    pool = sum(need) + extra_blocks
+    perm = torch.randperm(pool, generator=gl)
+    bt = torch.full((S, max(1, max(need or [1]))), -1, dtype=torch.int32)
+    off, slots = 0, []
+    for s, n in enumerate(need):
+        bt[s, :n] = perm[off:off + n].to(torch.int32)
+        off += n
+        t = torch.arange(ctx_lens[s], ctx_lens[s] + q_lens[s])
+        slots.append(bt[s, t // BS].long() * BS + t % BS)
+    T = sum(q_lens)
+    dev = torch.device(device)
+    query = torch.randn((T, H, D), generator=g, dtype=torch.float32, device=dev).to(dt)
+    key = torch.randn((T, KVH, D), generator=g, dtype=torch.float32, device=dev).to(dt)
+    value = torch.randn((T, KVH, D), generator=g, dtype=torch.float32, device=dev).to(dt)
+    key_cache = torch.randn((pool, KVH, D // x, BS, x), generator=g, dtype=torch.float32, device=dev).to(dt)
+    value_cache = torch.randn((pool, KVH, D, BS), generator=g, dtype=torch.float32, device=dev).to(dt)
+    slot_mapping = torch.cat(slots) if slots else torch.empty(0, dtype=torch.int64)
+    # chunk slots (and unused slots) poisoned: the context is the only valid cache content
+    nan = torch.tensor(float("nan"), dtype=dt, device=dev)
+    valid = torch.zeros(pool * BS, dtype=torch.bool)
+    for s in range(S):
+        t = torch.arange(ctx_lens[s])
+        valid[(bt[s, t // BS].long() * BS + t % BS)] = True
+    inv = (~valid).nonzero().flatten()
+    if inv.numel():
+        b, o = (inv // BS).to(dev), (inv % BS).to(dev)
+        key_cache[b, :, :, o, :] = nan
+        value_cache[b, :, :, o] = nan
+    qsl = torch.tensor([0] + list(torch.cumsum(torch.tensor(q_lens, dtype=torch.int64), 0).tolist()),
+                       dtype=torch.int32)
+    return PrefixWorkload(query, key, value, key_cache, value_cache, bt.to(dev), qsl.to(dev),
+                          torch.tensor(ctx_lens, dtype=torch.int32).to(dev), slot_mapping.to(dev), KVH, BS,
+                          list(ctx_lens), list(q_lens))

@@ -83,6 +83,11 @@ def _load():
                 I, I, I, I,            # num_tokens, num_kv_heads, head_size, block_size
                 ctypes.c_int64, I]     # num_blocks, input dtype
             lib.oracle_reshape_and_cache.restype = I
+            lib.oracle_prefix_attention.argtypes = [
+                P, P, I, P, P, P, P, I,   # out, query, q_dtype, key, value, key_cache, value_cache, kv_dtype
+                P, I, P, P,               # block_tables, max_blocks_per_seq, query_start_loc, context_lens
+                I, I, I, I, I, F]         # num_seqs, num_heads, num_kv_heads, head_size, block_size, scale
+            lib.oracle_prefix_attention.restype = I
             _lib = lib
     return _lib
 
@@ -238,3 +243,27 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, block
     if rc != 0:
         raise ValueError(f"oracle_reshape_and_cache rejected its arguments (rc={rc})")
     return kc, vc
+
+
+def prefix_attention(query, key, value, key_cache, value_cache, block_tables, query_start_loc,
+                     context_lens, *, num_kv_heads, block_size, scale, q_dtype, kv_dtype):
+    """Paged prefix attention (chunked prefill) in float64: out [total_q, H, D].
+
+    Context tokens come from the paged caches, the chunk's own keys / values
+    from key, value [total_q, kv_h, d] (causal within the chunk)."""
+    q = _raw(query)
+    k = _raw(key)
+    v = _raw(value)
+    kc = _raw(key_cache)
+    vc = _raw(value_cache)
+    i32 = lambda t: np.ascontiguousarray(np.asarray(t.cpu() if hasattr(t, "cpu") else t, dtype=np.int32))
+    bt, qsl, cl = i32(block_tables), i32(query_start_loc), i32(context_lens)
+    T, H, D = (int(n) for n in query.shape)
+    out = np.full((T, H, D), np.nan)
+    rc = _load().oracle_prefix_attention(
+        _ptr(out), _ptr(q), int(q_dtype), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), int(kv_dtype),
+        _ptr(bt), bt.shape[1], _ptr(qsl), _ptr(cl), len(cl), H, int(num_kv_heads), D, int(block_size),
+        float(scale))
+    if rc != 0:
+        raise ValueError(f"oracle_prefix_attention rejected its arguments (rc={rc})")
+    return out

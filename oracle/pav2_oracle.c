@@ -479,3 +479,84 @@ int oracle_reshape_and_cache(
     }
     return 0;
 }
+
+/* ---- Paged prefix attention (chunked prefill) ----------------------------
+ *
+ * Page "paged_attn.py", _forward_prefix_pytorch: sequence i has context_lens[i]
+ * tokens already in the paged cache and a chunk of q_len_i new tokens
+ * (query rows query_start_loc[i] .. query_start_loc[i+1]-1).  Query token j
+ * of the chunk (absolute position ctx + j), head h, attends to every context
+ * token (all precede it) and to chunk tokens k <= j (the causal mask), with
+ * scores q . K * scale, softmax over all of them, times V.  The page streams
+ * the keys in tiles with an online softmax; that reaches exactly one softmax
+ * over all keys, which is what is computed here.  Context keys come from the
+ * cache (block_tables[i][t / bs], slot t % bs, the decode gather), chunk keys
+ * from key / value [total_q, kv_h, d]; kv head h / (H / kv_h).  The page uses
+ * scale = head_size^-0.5, no scales for the cache and no ALiBi.
+ */
+int oracle_prefix_attention(
+    double *out,                                   /* [total_q, H, D] */
+    const void *query, int q_dtype,                /* [total_q, H, D] */
+    const void *key, const void *value,            /* [total_q, KVH, D], q_dtype */
+    const void *key_cache, const void *value_cache, int kv_dtype,
+    const int32_t *block_tables, int max_blocks_per_seq,
+    const int32_t *query_start_loc, const int32_t *context_lens,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+    float scale) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return -1;
+    if (elem_size(kv_dtype) == 0 || elem_size(q_dtype) == 0 || block_size <= 0) return -1;
+    const int D = head_size, H = num_heads, KVH = num_kv_heads, gqa = H / KVH;
+    const int x = 16 / elem_size(kv_dtype);
+    if (D % x) return -1;
+    for (int i = 0; i < num_seqs; ++i) {
+        const int q0 = query_start_loc[i], ql = query_start_loc[i + 1] - q0, ctx = context_lens[i];
+        if (ql < 0 || ctx < 0) return -1;
+        const int nk = ctx + ql;
+        double *z = (double *)malloc(sizeof(double) * (nk > 0 ? nk : 1));
+        if (!z) return -2;
+        for (int j = 0; j < ql; ++j) {
+            for (int h = 0; h < H; ++h) {
+                const int g = h / gqa, L = ctx + j + 1;
+                double m = -INFINITY;
+                for (int t = 0; t < L; ++t) {
+                    double dot = 0.0;
+                    for (int i2 = 0; i2 < D; ++i2) {
+                        double q = dec(q_dtype, query, ((int64_t)(q0 + j) * H + h) * D + i2);
+                        double k;
+                        if (t < ctx) {
+                            int64_t blk = block_tables[(int64_t)i * max_blocks_per_seq + t / block_size];
+                            k = dec(kv_dtype, key_cache,
+                                    (((blk * KVH + g) * (D / x) + i2 / x) * block_size + t % block_size) * x + i2 % x);
+                        } else {
+                            k = dec(q_dtype, key, ((int64_t)(q0 + t - ctx) * KVH + g) * D + i2);
+                        }
+                        dot += q * k;
+                    }
+                    z[t] = dot * (double)scale;
+                    if (z[t] > m) m = z[t];
+                }
+                double l = 0.0;
+                for (int t = 0; t < L; ++t) {
+                    z[t] = exp(z[t] - m);
+                    l += z[t];
+                }
+                for (int i2 = 0; i2 < D; ++i2) {
+                    double acc = 0.0;
+                    for (int t = 0; t < L; ++t) {
+                        double v;
+                        if (t < ctx) {
+                            int64_t blk = block_tables[(int64_t)i * max_blocks_per_seq + t / block_size];
+                            v = dec(kv_dtype, value_cache, ((blk * KVH + g) * D + i2) * block_size + t % block_size);
+                        } else {
+                            v = dec(q_dtype, value, ((int64_t)(q0 + t - ctx) * KVH + g) * D + i2);
+                        }
+                        acc += z[t] * v;
+                    }
+                    out[((int64_t)(q0 + j) * H + h) * D + i2] = acc / l;
+                }
+            }
+        }
+        free(z);
+    }
+    return 0;
+}
