@@ -64,6 +64,8 @@ def load():
         L.pav2_plan.restype = I
         L.pav2_decode_kv.argtypes = [P, P, ctypes.c_int64, I, I, P]
         L.pav2_decode_kv.restype = I
+        L.pav2_paged_prefix_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P]
+        L.pav2_paged_prefix_attention.restype = I
         L.pav2_reshape_and_cache.argtypes = [P, P, P, P, P, I, F, F, I, I, I, I, I, I, P]
         L.pav2_reshape_and_cache.restype = I
         L.pav2_check_inputs.argtypes = [P, P, I, I, I, I, P, P]
@@ -234,6 +236,32 @@ def decode_kv(src, compute_dtype=None, stream=None):
                                _stream(src, stream))
     _check(rc)
     return dst.view(src.shape)
+
+
+def paged_prefix_attention(output, query, key_cache, value_cache, block_tables, query_start_loc,
+                           context_lens, max_query_len, max_seq_len, scale=None, stream=None) -> None:
+    """Paged prefix attention (pav2_paged_prefix_attention): the chunks' query
+    rows over their context plus the chunk itself (causal), all read from the
+    paged cache -- write the chunks' keys / values there first
+    (reshape_and_cache).  scale defaults to head_size ** -0.5."""
+    T, H, D = (int(v) for v in query.shape)
+    if tuple(output.shape) != (T, H, D) or output.dtype != query.dtype:
+        raise ValueError("output must match query in shape and dtype")
+    if key_cache.dim() != 5 or value_cache.dim() != 4:
+        raise ValueError("key_cache must be 5-D and value_cache 4-D")
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise ValueError("prefix attention takes caches of the query dtype")
+    NB, KVH, bs = int(value_cache.shape[0]), int(value_cache.shape[1]), int(value_cache.shape[3])
+    S = int(context_lens.numel())
+    if int(query_start_loc.numel()) != S + 1 or int(block_tables.shape[0]) != S:
+        raise ValueError("query_start_loc must be [num_seqs + 1] and block_tables [num_seqs, ...]")
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    rc = load().pav2_paged_prefix_attention(
+        _dev(output, "output"), _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _i32(block_tables, "block_tables"), _i32(query_start_loc, "query_start_loc"),
+        _i32(context_lens, "context_lens"), S, H, KVH, D, bs, NB, int(block_tables.shape[1]), int(max_query_len),
+        int(max_seq_len), sc, _dtype_code(query), _stream(query, stream))
+    _check(rc)
 
 
 def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, kv_cache_dtype="auto",

@@ -157,6 +157,8 @@ int run_phase1(float *exp_sums, float *max_logits, void *tmp_output, const void 
     p.block_tables = block_tables;
     p.seq_lens = seq_lens;
     p.alibi = alibi_slopes;
+    p.query_start_loc = nullptr;
+    p.context_lens = nullptr;
     p.num_seqs = sh.num_seqs;
     p.num_heads = sh.num_heads;
     p.num_kv_heads = sh.num_kv_heads;
@@ -193,6 +195,8 @@ int run_v1(void *output, const void *query, const void *key_cache, const void *v
     p.block_tables = block_tables;
     p.seq_lens = seq_lens;
     p.alibi = alibi_slopes;
+    p.query_start_loc = nullptr;
+    p.context_lens = nullptr;
     p.num_seqs = sh.num_seqs;
     p.num_heads = sh.num_heads;
     p.num_kv_heads = sh.num_kv_heads;
@@ -362,6 +366,65 @@ int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype
     return launch_status(pav2::launch_decode_kv(src, dst, n, (int)kv_dtype, (int)compute_dtype,
                                                 static_cast<hipStream_t>(stream)),
                          "decode_kv");
+}
+
+int pav2_paged_prefix_attention(void *output, const void *query, const void *key_cache,
+                                const void *value_cache, const int32_t *block_tables,
+                                const int32_t *query_start_loc, const int32_t *context_lens, int num_seqs,
+                                int num_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_query_len, int max_seq_len, float scale,
+                                pav2_dtype_t dtype, pav2_stream_t stream) {
+    g_err[0] = 0;
+    if (dtype == PAV2_FP8_E4M3)
+        return fail(PAV2_ERR_UNSUPPORTED, "prefix attention takes f32, f16 or bf16 caches of the query dtype");
+    if (max_query_len < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "max_query_len must be >= 0");
+    if (max_seq_len < max_query_len)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "max_seq_len %d < max_query_len %d", max_seq_len, max_query_len);
+    Shape sh{num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks, max_blocks_per_seq,
+             pav2_max_num_partitions(max_seq_len) > 0 ? pav2_max_num_partitions(max_seq_len) : 1, max_seq_len,
+             (int)dtype, (int)dtype};
+    int rc = check_shape(sh);
+    if (rc) return rc;
+    const int gqa = num_heads / num_kv_heads;
+    const int64_t row_blocks = ((int64_t)max_query_len * gqa + pav2::kMaxHeadsPerGroup - 1) / pav2::kMaxHeadsPerGroup;
+    const int64_t work = (int64_t)num_seqs * num_kv_heads * row_blocks;
+    if (work > ((int64_t)1 << 31) - 1 || row_blocks > ((int64_t)1 << 30))
+        return fail(PAV2_ERR_UNSUPPORTED, "num_seqs * num_kv_heads * row blocks = %lld is too large", (long long)work);
+    if (work == 0) return PAV2_OK;
+    if (!output || !query || !key_cache || !value_cache || !block_tables || !query_start_loc || !context_lens)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    pav2::Phase1Params p;
+    p.tmp_out = output;
+    p.exp_sums = nullptr;
+    p.max_logits = nullptr;
+    p.query = query;
+    p.key_cache = static_cast<const uint8_t *>(key_cache);
+    p.value_cache = static_cast<const uint8_t *>(value_cache);
+    p.block_tables = block_tables;
+    p.seq_lens = nullptr;
+    p.alibi = nullptr;
+    p.query_start_loc = query_start_loc;
+    p.context_lens = context_lens;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.gqa = gqa;
+    p.head_groups = (int)row_blocks;
+    p.bs_log2 = ilog2_exact(block_size);
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_num_partitions = sh.max_num_partitions;
+    p.num_work = (int)work;
+    p.sched = 3;
+    p.head_stride = (int64_t)head_size * block_size * elem_bytes(dtype);
+    p.blk_stride = p.head_stride * num_kv_heads;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.v_scale = 1.0f;
+    // 16 rows per group, no partition-count prefix
+    const int lds = pav2::phase1_lds_bytes(pav2::kMaxHeadsPerGroup, head_size, pav2::kPhase1Waves, p.bs_log2,
+                                           num_seqs, false);
+    return launch_status(pav2::launch_phase1(p, (int)dtype, (int)dtype, head_size, pav2::kPhase1Waves, lds,
+                                             static_cast<hipStream_t>(stream)),
+                         "prefix attention");
 }
 
 int pav2_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,

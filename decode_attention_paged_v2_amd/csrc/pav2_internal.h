@@ -42,6 +42,8 @@ struct Phase1Params {
     const int32_t *block_tables;   // [S, MBPS]
     const int32_t *seq_lens;       // [S]
     const float *alibi;            // [H] or null
+    const int32_t *query_start_loc;  // prefix attention: [S + 1] first query row of each chunk
+    const int32_t *context_lens;     // prefix attention: [S] tokens before each chunk
     int num_seqs, num_heads, num_kv_heads;
     int gqa;                       // num_heads / num_kv_heads
     int head_groups;               // ceil(gqa / 16)
@@ -49,7 +51,8 @@ struct Phase1Params {
     int max_blocks_per_seq;
     int max_num_partitions;
     int num_work;                  // S * KVH * head_groups * maxP (single pass: without maxP)
-    int sched;                     // 0 dense slots, 1 compact list of used partitions, 2 single pass
+    int sched;                     // 0 dense slots, 1 compact list of used partitions, 2 single pass,
+                                   // 3 prefix attention (head_groups = row blocks of 16)
     int64_t blk_stride;            // bytes per physical block (all kv heads)
     int64_t head_stride;           // bytes per (block, kv head)
     float scale_log2;              // scale * k_scale * log2(e)

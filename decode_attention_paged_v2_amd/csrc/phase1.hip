@@ -158,7 +158,11 @@ template <int QDT, int KVDT, int D, int WAVES, int SCHED, int BS>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(kPhase1Occupancy)))
 phase1_kernel(const Phase1Params P) {
     constexpr bool COMPACT = SCHED == 1;
-    constexpr bool SINGLE = SCHED == 2;
+    // Paged prefix attention: the 16 columns of a group are (query token,
+    // head) rows of one chunk, each with its own causal limit, walked like
+    // the single pass over the partitions of the sequence.
+    constexpr bool PREFIX = SCHED == 3;
+    constexpr bool SINGLE = SCHED == 2 || PREFIX;
     using S = Shape<QDT, KVDT, D>;
     constexpr int NKL = S::kKLoads;
     constexpr int NDT = S::kDTiles;
@@ -173,7 +177,7 @@ phase1_kernel(const Phase1Params P) {
     const int maxP = P.max_num_partitions;
     const int HG = P.head_groups;
     const int KVH = P.num_kv_heads;
-    const int heads_alloc = min(P.gqa, kMaxHeadsPerGroup);
+    const int heads_alloc = PREFIX ? kMaxHeadsPerGroup : min(P.gqa, kMaxHeadsPerGroup);
     constexpr int kBsLog2 = BS == 16 ? 4 : (BS == 32 ? 5 : -1);
     const int bs_log2 = kBsLog2 >= 0 ? kBsLog2 : P.bs_log2;
     const int bs_mask = (1 << bs_log2) - 1;
@@ -195,10 +199,25 @@ phase1_kernel(const Phase1Params P) {
     // the workgroups of one XCD (blockIdx % 8) take one contiguous block of it.
     // Single pass: the items are the partitions of one (seq, kv head, head
     // group), blockIdx.x, taken in order.
+    // Prefix attention: workgroup (sequence, kv head, block of 16 rows), row
+    // rr = token j * gqa + head r of the chunk; the block walks the
+    // partitions up to its last row's limit context + j + 1.
+    int pf_q0 = 0, pf_ctx = 0, pf_rows = 0, pf_lmax = 0;
     int item, item_end;
     if constexpr (SINGLE) {
         if ((int)blockIdx.x >= P.num_work) return;
-        const int L = P.seq_lens[blockIdx.x / (KVH * HG)];
+        int L;
+        if constexpr (PREFIX) {
+            const int sq = blockIdx.x / (KVH * HG), rb = blockIdx.x % HG;
+            pf_q0 = P.query_start_loc[sq];
+            pf_rows = (P.query_start_loc[sq + 1] - pf_q0) * P.gqa;
+            pf_ctx = P.context_lens[sq];
+            if (rb * kMaxHeadsPerGroup >= pf_rows) return;   // no rows in this block (uniform)
+            pf_lmax = pf_ctx + (min(pf_rows, (rb + 1) * kMaxHeadsPerGroup) - 1) / P.gqa + 1;
+            L = pf_lmax;
+        } else {
+            L = P.seq_lens[blockIdx.x / (KVH * HG)];
+        }
         item = 0;
         item_end = L > 0 ? (L + kPartition - 1) / kPartition : 0;
     } else if constexpr (COMPACT) {
@@ -305,10 +324,11 @@ phase1_kernel(const Phase1Params P) {
     const int col = lane & 15;   // token row (K^T loads), head column (outputs), head-dim row (V^T loads)
     const int grp = lane >> 4;   // 4-element slice index within the MFMA operand
 
-    const int L = P.seq_lens[s];
+    const int L = PREFIX ? pf_lmax : P.seq_lens[s];
     const int start = p * kPartition;
     const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
-    const int nh = min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
+    const int nh = PREFIX ? min(kMaxHeadsPerGroup, pf_rows - hg * kMaxHeadsPerGroup)
+                          : min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
 
     if (start >= L) {   // unused partition slot (dense and compact schedules)
         if (!SINGLE && tid < nh) {
@@ -332,8 +352,19 @@ phase1_kernel(const Phase1Params P) {
     // Query operand (B of S^T = K Q^T): head h0 + col, head-dim slice of K vector
     // (4u + grp), i.e. elements d = X * (4u + grp) + e.
     const bool hvalid = col < nh;
-    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(P.query) +
-                          (((int64_t)s * P.num_heads + h0 + col) * D) * QB;
+    const uint8_t *qrow;
+    int lcol = L;   // prefix attention: this lane's column's causal limit (keys t < lcol)
+    if constexpr (PREFIX) {
+        const int rr = hg * kMaxHeadsPerGroup + col;
+        const int j = rr / P.gqa;
+        qrow = reinterpret_cast<const uint8_t *>(P.query) +
+               (((int64_t)(pf_q0 + j) * P.num_heads + g * P.gqa + (rr - j * P.gqa)) * D) * QB;
+        lcol = hvalid ? pf_ctx + j + 1 : L;
+    } else {
+        qrow = reinterpret_cast<const uint8_t *>(P.query) + (((int64_t)s * P.num_heads + h0 + col) * D) * QB;
+    }
+    // the block's smallest column limit (its first row's): units below it need no mask
+    const int lmin = PREFIX ? pf_ctx + (hg * kMaxHeadsPerGroup) / P.gqa + 1 : L;
     Words<X * QB / 4> qw[NKL];
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
@@ -535,8 +566,8 @@ phase1_kernel(const Phase1Params P) {
         for (int e = 0; e < 8; ++e)
             sc[u][e] = fmaf(sc[u][e], scale_log2, e == 0 ? bu : fmaf(slope2, (float)e, bu));
         const int tu = start + unit_of(u) * UNIT;   // unclamped first token of the unit
-        if (tu + UNIT > L) {
-            const int nv = L - (tu + 8 * grp);      // valid tokens among the lane's 8
+        if (tu + UNIT > lmin) {
+            const int nv = lcol - (tu + 8 * grp);   // valid tokens among the lane's 8
 #pragma unroll
             for (int e = 0; e < 8; ++e) sc[u][e] = e < nv ? sc[u][e] : -INFINITY;
         }
@@ -704,7 +735,7 @@ phase1_kernel(const Phase1Params P) {
                 const int d0 = (idx - hh * PER_HEAD) * VEC;
                 float M, l, lr, a[VEC];
                 combine(hh, d0, M, l, lr, a);
-                if (P.alibi != nullptr) M += P.alibi[h0 + hh] * kLog2e * (float)last;
+                if (!PREFIX && P.alibi != nullptr) M += P.alibi[h0 + hh] * kLog2e * (float)last;
                 const float Mn = fmaxf(run_m[k], M);
                 const float fo = exp2_fast(run_m[k] - Mn);   // 0 for the first partition
                 const float fn = exp2_fast(M - Mn);
@@ -747,7 +778,8 @@ phase1_kernel(const Phase1Params P) {
     if constexpr (SINGLE) {   // the normalised output, written once (zero rows for an empty sequence)
         const int hg = blockIdx.x % HG, g = (blockIdx.x / HG) % KVH, s = blockIdx.x / (HG * KVH);
         const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
-        const int nh = min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
+        const int nh = PREFIX ? min(kMaxHeadsPerGroup, pf_rows - hg * kMaxHeadsPerGroup)
+                              : min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
 #pragma unroll
         for (int k = 0; k < NRUN; ++k) {
             const int idx = tid0 + k * WAVES * 64;
@@ -758,8 +790,13 @@ phase1_kernel(const Phase1Params P) {
                 float r[VEC];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) r[e] = run_o[k][e] * inv;
-                uint8_t *dst = reinterpret_cast<uint8_t *>(P.tmp_out) +
-                               (((int64_t)s * P.num_heads + h0 + hh) * D + d0) * QB;
+                int64_t orow = (int64_t)s * P.num_heads + h0 + hh;   // output row (token, head)
+                if constexpr (PREFIX) {
+                    const int rr = hg * kMaxHeadsPerGroup + hh;
+                    const int j = rr / P.gqa;
+                    orow = (int64_t)(pf_q0 + j) * P.num_heads + g * P.gqa + (rr - j * P.gqa);
+                }
+                uint8_t *dst = reinterpret_cast<uint8_t *>(P.tmp_out) + (orow * D + d0) * QB;
                 if constexpr (QDT == F32) {
                     *reinterpret_cast<f32x4 *>(dst) = f32x4{r[0], r[1], r[2], r[3]};
                 } else {
@@ -814,8 +851,8 @@ hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
             per_cu = 1;
         const int cap = kPhase1CompactRounds * device_cu_count() * per_cu;
         grid = grid < cap ? grid : cap;
-    } else if (SCHED == 2) {
-        grid = p.num_work;   // one workgroup per (sequence, kv head, head group)
+    } else if (SCHED >= 2) {
+        grid = p.num_work;   // one workgroup per (sequence, kv head, head or row group)
     }
     hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, SCHED, BS>), dim3(grid), dim3(WAVES * 64), lds,
                        stream, p);
@@ -841,6 +878,9 @@ hipError_t launch_one(const Phase1Params &p, int lds, hipStream_t stream) {
     case 0: return launch_bs<QDT, KVDT, D, 0>(p, lds, stream);
     case 1: return launch_bs<QDT, KVDT, D, 1>(p, lds, stream);
     case 2: return launch_bs<QDT, KVDT, D, 2>(p, lds, stream);
+    case 3:
+        if constexpr (QDT == KVDT) return launch_bs<QDT, KVDT, D, 3>(p, lds, stream);   // 16/32-bit caches
+        else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }

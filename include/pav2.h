@@ -203,6 +203,41 @@ int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype
                    pav2_dtype_t compute_dtype, pav2_stream_t stream);
 
 /*
+ * Paged prefix attention for chunked prefill (page "paged_attn.py",
+ * forward_prefix / _forward_prefix_pytorch): sequence i has context_lens[i]
+ * tokens already in the cache and a chunk of new query tokens, rows
+ * query_start_loc[i] .. query_start_loc[i+1]-1 of `query`.  Chunk token j
+ * (absolute position context_lens[i] + j), head h, attends to the context and
+ * to chunk tokens k <= j (causal):
+ *
+ *   out[q, h] = softmax_t(scale * q . K_t) V_t,  t <= context_lens[i] + j,
+ *
+ * with K_t, V_t of kv head h / (num_heads / num_kv_heads) read from the paged
+ * cache through block_tables[i] (the decode gather).  The chunk's own keys
+ * and values must already be in the cache at their positions (written by
+ * pav2_reshape_and_cache, as a backend does before attention); for caches of
+ * the query dtype with unit scales that is bit for bit the page's reading of
+ * them from the key / value tensors.  The page uses scale = head_size^-0.5.
+ *
+ *   output, query  [total_query_tokens, num_heads, head_size]  dtype
+ *   key_cache, value_cache as for decode, dtype (no fp8, no k/v scales)
+ *   block_tables [num_seqs, max_blocks_per_seq] int32, covering context + chunk
+ *   query_start_loc [num_seqs + 1] int32, context_lens [num_seqs] int32
+ *
+ * max_query_len >= every chunk's length and max_seq_len >= every context +
+ * chunk length (host values sizing the grid and validating the table width).
+ * One workgroup per (sequence, kv head, 16 (token, head) rows) walks the
+ * 512-token partitions up to its rows' causal limit, as the single pass does.
+ * No ALiBi or sliding window (the page's fallback applies neither).
+ */
+int pav2_paged_prefix_attention(
+    void *output, const void *query, const void *key_cache, const void *value_cache,
+    const int32_t *block_tables, const int32_t *query_start_loc, const int32_t *context_lens,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+    int num_blocks, int max_blocks_per_seq, int max_query_len, int max_seq_len,
+    float scale, pav2_dtype_t dtype, pav2_stream_t stream);
+
+/*
  * KV-cache write (page "paged_attn.py", write_to_paged_cache, which passes
  * key, value, key_cache, value_cache, slot_mapping, kv_cache_dtype, k_scale
  * and v_scale to reshape_and_cache): stores the keys and values of

@@ -253,3 +253,26 @@ def test_reshape_and_cache_binding_checks_shapes():
     with pytest.raises(ValueError, match="device tensor"):
         pav2.reshape_and_cache(k, k, torch.zeros(4, 2, 16, 16, 4), torch.zeros(4, 2, 64, 16),
                                torch.zeros(3, dtype=torch.int64))
+
+
+def test_prefix_attention_validation():
+    lib = pav2.load()
+    v = ctypes.c_void_p(16)
+
+    def call(**over):
+        a = dict(output=v, query=v, key_cache=v, value_cache=v, block_tables=v, query_start_loc=v,
+                 context_lens=v, num_seqs=4, num_heads=24, num_kv_heads=4, head_size=256, block_size=16,
+                 num_blocks=1000, max_blocks_per_seq=1100, max_query_len=512, max_seq_len=17000,
+                 scale=0.0625, dtype=B.BF16, stream=None)
+        a.update(over)
+        return lib.pav2_paged_prefix_attention(*a.values())
+    assert call(dtype=B.FP8_E4M3) == -2
+    assert call(num_heads=25) == -1
+    assert call(head_size=100) == -2
+    assert call(block_size=24) == -1
+    assert call(max_query_len=-1) == -1
+    assert call(max_seq_len=100) == -1                 # shorter than the chunk
+    assert call(max_blocks_per_seq=10) == -1           # table narrower than ceil(max_seq_len / 16)
+    assert call(context_lens=None) == -1
+    assert call(num_seqs=0, output=None, query=None) == 0   # nothing to do
+    assert call(max_query_len=0, output=None) == 0

@@ -1,0 +1,119 @@
+"""Paged prefix attention on the GPU (pav2_paged_prefix_attention through the C
+ABI) against the oracle.
+
+The chunks' keys and values are first written into the device cache with
+pav2_reshape_and_cache (as a backend does before attention); the oracle
+reads them from the key / value tensors instead, as the page's fallback does.
+Every other cache slot the chunks do not cover holds NaN, so a read of an
+unwritten or foreign slot shows up.  Tolerances as for decode: 2e-3 (16-bit)
+or one ulp of the output dtype where that is larger, 2e-5 for f32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import decode_attention_paged_v2_amd as pav2
+from decode_attention_paged_v2_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+_CODE = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}
+_TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TOL = {"f32": 2e-5, "f16": 2e-3, "bf16": 2e-3}
+MANT = {"f32": 23, "f16": 10, "bf16": 7}
+
+
+def run_case(ctx, ql, H, KVH, d, BS, dtype, seed=0):
+    pw = W.prefix_workload(ctx, ql, H, KVH, d, BS, dtype=dtype, seed=seed)
+    scale = d ** -0.5
+    ref = oracle.prefix_attention(pw.query, pw.key, pw.value, pw.key_cache, pw.value_cache, pw.block_tables,
+                                  pw.query_start_loc, pw.context_lens, num_kv_heads=KVH, block_size=BS,
+                                  scale=scale, q_dtype=_CODE[dtype], kv_dtype=_CODE[dtype])
+    g = pw.to(DEV)
+    pav2.reshape_and_cache(g.key, g.value, g.key_cache, g.value_cache, g.slot_mapping)
+    out = torch.full_like(g.query, float("nan"))
+    pav2.paged_prefix_attention(out, g.query, g.key_cache, g.value_cache, g.block_tables, g.query_start_loc,
+                                g.context_lens, max(ql) if ql else 0, max(c + q for c, q in zip(ctx, ql)),
+                                scale=scale)
+    torch.cuda.synchronize()
+    return out.cpu(), ref
+
+
+def assert_close(out, ref, dtype):
+    r = torch.from_numpy(ref).to(_TD[dtype]).double().numpy()     # the reference rounded to the output dtype
+    got = out.double().numpy()
+    assert np.isfinite(got).all()
+    a = np.maximum(np.abs(r), 2.0 ** -126)
+    allowed = np.maximum(TOL[dtype], 2.0 ** (np.floor(np.log2(a)) - MANT[dtype]))
+    err = np.abs(got - r)
+    worst = np.max(err - allowed)
+    assert worst <= 0, f"max error {err.max():.3g} beyond tolerance"
+    return float(err.max())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 80, 128, 256])
+def test_prefix_matches_oracle(dtype, d):
+    print(f"case prefix {dtype} d={d}", flush=True)
+    # contexts: none, under one tile, one partition, several partitions; chunks of 1 .. 70 tokens, one empty
+    ctx, ql = [0, 5, 512, 700, 1100, 33], [7, 1, 16, 33, 70, 0]
+    out, ref = run_case(ctx, ql, 12, 2, d, 16, dtype, seed=d)
+    assert_close(out, ref, dtype)
+
+
+@pytest.mark.parametrize("H,KVH", [(4, 4), (8, 1), (24, 4), (32, 1)])
+def test_prefix_gqa_row_blocks(H, KVH):
+    """Blocks of 16 (token, head) rows that cut across tokens (gqa 6) or hold one head only (gqa 1)."""
+    print(f"case prefix gqa H={H} KVH={KVH}", flush=True)
+    out, ref = run_case([300, 0, 1030], [21, 40, 9], H, KVH, 128, 16, "bf16", seed=H + KVH)
+    assert_close(out, ref, "bf16")
+
+
+@pytest.mark.parametrize("BS", [8, 32, 64, 512])
+def test_prefix_block_sizes(BS):
+    print(f"case prefix block {BS}", flush=True)
+    out, ref = run_case([17, 600], [30, 12], 8, 2, 64, BS, "bf16", seed=BS)
+    assert_close(out, ref, "bf16")
+
+
+def test_prefix_chunk_longer_than_a_partition():
+    """A chunk spanning several partitions: rows' causal limits fall in different partitions."""
+    print("case prefix long chunk", flush=True)
+    out, ref = run_case([100], [1100], 4, 1, 64, 16, "bf16", seed=9)
+    assert_close(out, ref, "bf16")
+
+
+def test_prefix_medium_gqa6_d256():
+    """The long-context layout (24 query heads over 4 kv heads, d = 256, bf16) at a size the oracle finishes."""
+    print("case prefix medium", flush=True)
+    out, ref = run_case([1500, 700], [96, 40], 24, 4, 256, 16, "bf16", seed=11)
+    assert_close(out, ref, "bf16")
+
+
+def test_prefix_one_token_chunks_match_decode_oracle():
+    """One-token chunks are decode steps: compared with the decode oracle on the written cache."""
+    pw = W.prefix_workload([37, 600, 0], [1, 1, 1], 6, 2, 128, 16, dtype="bf16", seed=12)
+    g = pw.to(DEV)
+    pav2.reshape_and_cache(g.key, g.value, g.key_cache, g.value_cache, g.slot_mapping)
+    out = torch.full_like(g.query, float("nan"))
+    pav2.paged_prefix_attention(out, g.query, g.key_cache, g.value_cache, g.block_tables, g.query_start_loc,
+                                g.context_lens, 1, 601)
+    kb, vb = oracle.reshape_and_cache(pw.key, pw.value, pw.key_cache, pw.value_cache, pw.slot_mapping,
+                                      block_size=16, cache_dtype=oracle.BF16)
+    kc = torch.from_numpy(kb).view(torch.bfloat16).reshape(pw.key_cache.shape)
+    vc = torch.from_numpy(vb).view(torch.bfloat16).reshape(pw.value_cache.shape)
+    ref = oracle.dense_attention(pw.query, kc, vc, pw.block_tables, torch.tensor([38, 601, 1], dtype=torch.int32),
+                                 num_kv_heads=2, scale=128 ** -0.5, block_size=16, q_dtype=oracle.BF16,
+                                 kv_dtype=oracle.BF16)
+    torch.cuda.synchronize()
+    assert_close(out.cpu(), ref, "bf16")
+
+
+def test_prefix_rejects_fp8_cache():
+    pw = W.prefix_workload([4], [2], 4, 4, 64, 16, dtype="bf16").to(DEV)
+    kc = pw.key_cache.to(torch.float8_e4m3fn)
+    with pytest.raises(ValueError):
+        pav2.paged_prefix_attention(torch.empty_like(pw.query), pw.query, kc, pw.value_cache, pw.block_tables,
+                                    pw.query_start_loc, pw.context_lens, 2, 6)
