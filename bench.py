@@ -193,6 +193,69 @@ def cache_write_bench(args, dev):
     return result
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFIX_CASE = dict(ctx=[16384] * 4, ql=[512] * 4, H=24, KVH=4, d=256, bs=16, dtype="bf16", seed=1006)
+
+
+def prefix_flops(ctx, ql, H, d):
+    """4 d flops (q.K and p.V) per visible (row, key) pair: row (j, h) sees ctx + j + 1 keys."""
+    return sum(4 * d * H * (q * c + q * (q + 1) // 2) for c, q in zip(ctx, ql))
+
+
+def prefix_bench(args, dev):
+    """Paged prefix attention over a chunked prefill (the chunk's keys and
+    values written into the cache first, outside the timed region)."""
+    pav2.load()
+    c = PREFIX_CASE
+    pw = W.prefix_workload(c["ctx"], c["ql"], c["H"], c["KVH"], c["d"], c["bs"], dtype=c["dtype"], seed=c["seed"],
+                           device=dev)
+    pav2.reshape_and_cache(pw.key, pw.value, pw.key_cache, pw.value_cache, pw.slot_mapping)
+    out = torch.empty_like(pw.query)
+    max_seq = max(a + b for a, b in zip(c["ctx"], c["ql"]))
+    stream = torch.cuda.current_stream(dev)
+    fn = lambda: pav2.paged_prefix_attention(out, pw.query, pw.key_cache, pw.value_cache, pw.block_tables,
+                                             pw.query_start_loc, pw.context_lens, max(c["ql"]), max_seq)
+    mean, mn, wall = _time_launches(fn, args.steps, args.warmup, stream)
+    flops = prefix_flops(c["ctx"], c["ql"], c["H"], c["d"])
+    eb = 2 if c["dtype"] != "f32" else 4
+    kv_bytes = sum((a + b) for a, b in zip(c["ctx"], c["ql"])) * c["KVH"] * 2 * c["d"] * eb
+    tflops = flops / (mean * 1e-3) / 1e12
+    result = {
+        "metric": "paged prefix attention TFLOP/s (chunked prefill) and % of bf16 MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(mean, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c["dtype"], "data": "synthetic",
+        "config": {"workload": "4 seqs x (16384 cached + 512 new tokens), H=24, kv_h=4 (GQA 6), d=256, bf16, "
+                               "block 16", "num_seqs": 4, "context": 16384, "chunk": 512},
+        "ms_min": round(mn, 5), "wall_ms_per_launch": round(wall, 5),
+        "kv_GBps_if_read_once": round(kv_bytes / (mean * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "phase1_kernel (prefix)", "algorithmic_flops_per_launch": flops},
+        "library": pav2.lib_path(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefix_cpu_baseline(pw, c)
+    return result
+
+
+def prefix_cpu_baseline(pw, c, n_rows=12):
+    """The oracle on the first n_rows chunk tokens of sequence 0 (one host thread)."""
+    import oracle
+    host = pw.to("cpu")
+    n = n_rows
+    t0 = time.perf_counter()
+    oracle.prefix_attention(host.query[:n], host.key[:n], host.value[:n], host.key_cache, host.value_cache,
+                            host.block_tables[:1], torch.tensor([0, n], dtype=torch.int32), host.context_lens[:1],
+                            num_kv_heads=c["KVH"], block_size=c["bs"], scale=c["d"] ** -0.5,
+                            q_dtype=oracle.BF16, kv_dtype=oracle.BF16)
+    dt = time.perf_counter() - t0
+    flops = prefix_flops([c["ctx"][0]], [n], c["H"], c["d"])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} chunk tokens of sequence 0 (all 24 heads), float64 C oracle, {dt:.2f} s wall",
+            "seconds": round(dt, 3)}
+
+
 def measured_cache_traffic(config):
     """HBM bytes per cache-write launch from the committed counter summary, or
     None when there is none or it was taken on different kernel sources."""
@@ -237,11 +300,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="extra per-step timings with a 1 GiB cache flush before each step")
-    ap.add_argument("--mode", default="decode", choices=["decode", "copy", "cache_write"],
+    ap.add_argument("--mode", default="decode", choices=["decode", "copy", "cache_write", "prefix"],
                     help="copy: time a plain 1 GiB device copy (the reference kernel for "
                          "scaling HBM byte counters and for achievable bandwidth); cache_write: "
                          "time the KV-cache write of the workload's whole context (and of one "
-                         "decode step's tokens)")
+                         "decode step's tokens); prefix: time paged prefix attention for a "
+                         "chunked prefill")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -259,6 +323,9 @@ def main():
         return
     if args.mode == "cache_write":
         print(json.dumps(cache_write_bench(args, dev)), flush=True)
+        return
+    if args.mode == "prefix":
+        print(json.dumps(prefix_bench(args, dev)), flush=True)
         return
     pav2.load()
     spec = W.SPECS[args.config]

@@ -89,7 +89,9 @@ def _kind(name: str) -> str:
 def _bench_args(config: str, mode: str, steps: int, warmup: int) -> list:
     args = [sys.executable, BENCH, "--config", config, "--steps", str(steps), "--warmup", str(warmup),
             "--no-cpu-baseline"]
-    return args + (["--mode", "cache_write"] if mode == "cache_write" else ["--flush-steps", "0"])
+    if mode in ("cache_write", "prefix"):
+        return args + ["--mode", mode]
+    return args + ["--flush-steps", "0"]
 
 
 def kernel_trace(config: str, out: str, steps: int = 10, mode: str = "decode") -> dict:
@@ -310,10 +312,38 @@ def write_cache_summary(config: str, out: str, trace: dict, counters: dict | Non
     return os.path.join(out, name + ".md")
 
 
+def write_prefix_summary(out: str, trace: dict) -> str:
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_for_counts", BENCH)
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    c = bench.PREFIX_CASE
+    flops = bench.prefix_flops(c["ctx"], c["ql"], c["H"], c["d"])
+    t = trace["phase1"]
+    tf = flops / (t["avg_us"] * 1e-6) / 1e12
+    name = "prefix_attention"
+    lines = ["# Paged prefix attention profile: 4 seqs x (16384 cached + 512 new tokens), H=24, kv_h=4, d=256, bf16",
+             "", f"Kernel sources hash: `{source_hash('decode')}`", "",
+             "Command (from the repository root):", "",
+             "    python -m decode_attention_paged_v2_amd.rocprof_harness --mode prefix --out gpurun_out/prof", "",
+             "which runs:", "", "    " + trace["command"], "",
+             "| kernel | calls | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|",
+             f"| `{t['name'][:90]}` | {t['calls']} | {t['avg_us']:.2f} | {t['min_us']:.2f} | {t['max_us']:.2f} |", "",
+             f"Algorithmic flops per launch (4 d per visible (row, key) pair): {flops:,}; at the average duration "
+             f"that is {tf:.1f} TFLOP/s = {100 * tf / 2500:.2f} % of the 2.5 PFLOP/s bf16 MFMA peak."]
+    data = {"source_hash": source_hash("decode"), "trace": trace, "algorithmic_flops": flops, "achieved_TFLOPs": tf,
+            "taken": time.strftime("%Y-%m-%d %H:%M:%S")}
+    with open(os.path.join(out, name + ".md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    with open(os.path.join(out, name + ".json"), "w") as fh:
+        json.dump(data, fh, indent=1)
+    return os.path.join(out, name + ".md")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="long_gqa")
-    ap.add_argument("--mode", default="decode", choices=["decode", "cache_write"])
+    ap.add_argument("--mode", default="decode", choices=["decode", "cache_write", "prefix"])
     ap.add_argument("--out", default="gpurun_out/prof")
     ap.add_argument("--pmc", action="store_true", help="HBM FETCH_SIZE / WRITE_SIZE passes")
     ap.add_argument("--sq", action="store_true", help="instruction-mix / utilisation passes")
@@ -322,6 +352,10 @@ def main():
     out = os.path.abspath(a.out)
     os.makedirs(out, exist_ok=True)
     trace = kernel_trace(a.config, out, a.steps, a.mode)
+    if a.mode == "prefix":
+        path = write_prefix_summary(out, trace)
+        print(open(path).read(), flush=True)
+        return
     counters = pmc(a.config, out, a.mode) if a.pmc else None
     if a.mode == "cache_write":
         path = write_cache_summary(a.config, out, trace, counters)
