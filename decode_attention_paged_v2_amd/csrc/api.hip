@@ -386,7 +386,7 @@ int pav2_paged_prefix_attention(void *output, const void *query, const void *key
     int rc = check_shape(sh);
     if (rc) return rc;
     const int gqa = num_heads / num_kv_heads;
-    const int64_t row_blocks = ((int64_t)max_query_len * gqa + pav2::kMaxHeadsPerGroup - 1) / pav2::kMaxHeadsPerGroup;
+    const int64_t row_blocks = ((int64_t)max_query_len * gqa + pav2::kPrefixRows - 1) / pav2::kPrefixRows;
     const int64_t work = (int64_t)num_seqs * num_kv_heads * row_blocks;
     if (work > ((int64_t)1 << 31) - 1 || row_blocks > ((int64_t)1 << 30))
         return fail(PAV2_ERR_UNSUPPORTED, "num_seqs * num_kv_heads * row blocks = %lld is too large", (long long)work);
@@ -419,7 +419,7 @@ int pav2_paged_prefix_attention(void *output, const void *query, const void *key
     p.blk_stride = p.head_stride * num_kv_heads;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.v_scale = 1.0f;
-    // 16 rows per group, no partition-count prefix
+    // 16 rows per wavefront, no partition-count prefix
     const int lds = pav2::phase1_lds_bytes(pav2::kMaxHeadsPerGroup, head_size, pav2::kPhase1Waves, p.bs_log2,
                                            num_seqs, false);
     return launch_status(pav2::launch_phase1(p, (int)dtype, (int)dtype, head_size, pav2::kPhase1Waves, lds,

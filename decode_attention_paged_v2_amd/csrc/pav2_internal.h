@@ -52,7 +52,7 @@ struct Phase1Params {
     int max_num_partitions;
     int num_work;                  // S * KVH * head_groups * maxP (single pass: without maxP)
     int sched;                     // 0 dense slots, 1 compact list of used partitions, 2 single pass,
-                                   // 3 prefix attention (head_groups = row blocks of 16)
+                                   // 3 prefix attention (head_groups = blocks of kPrefixRows rows)
     int64_t blk_stride;            // bytes per physical block (all kv heads)
     int64_t head_stride;           // bytes per (block, kv head)
     float scale_log2;              // scale * k_scale * log2(e)
@@ -93,6 +93,10 @@ hipError_t launch_check_inputs(const int32_t *block_tables, const int32_t *seq_l
 #define PAV2_PHASE1_NONTEMPORAL 1
 #endif
 constexpr int kPhase1Waves = PAV2_PHASE1_WAVES;
+// Prefix attention: rows (query token, head) per workgroup, 16 per
+// wavefront, and the key slice all wavefronts take per step (their 4 units).
+constexpr int kPrefixRows = kPhase1Waves * kMaxHeadsPerGroup;
+constexpr int kPrefixSlice = kPartition / kPhase1Waves;
 constexpr int kPhase1Occupancy = PAV2_PHASE1_OCCUPANCY;
 constexpr bool kPhase1NonTemporal = PAV2_PHASE1_NONTEMPORAL != 0;
 constexpr int kPhase2Threads = 256;

@@ -199,9 +199,12 @@ phase1_kernel(const Phase1Params P) {
     // the workgroups of one XCD (blockIdx % 8) take one contiguous block of it.
     // Single pass: the items are the partitions of one (seq, kv head, head
     // group), blockIdx.x, taken in order.
-    // Prefix attention: workgroup (sequence, kv head, block of 16 rows), row
-    // rr = token j * gqa + head r of the chunk; the block walks the
-    // partitions up to its last row's limit context + j + 1.
+    // Prefix attention: workgroup (sequence, kv head, block of 64 rows), row
+    // rr = token j * gqa + head r of the chunk; wavefront w owns rows
+    // 16 w .. 16 w + 15 of the block.  All four wavefronts take the same
+    // 128-token slice per item (so each K/V vector is fetched once for 64
+    // rows) up to the block's last row's limit context + j + 1, each keeping
+    // its rows' running (max, sum, output) in registers.
     int pf_q0 = 0, pf_ctx = 0, pf_rows = 0, pf_lmax = 0;
     int item, item_end;
     if constexpr (SINGLE) {
@@ -212,14 +215,15 @@ phase1_kernel(const Phase1Params P) {
             pf_q0 = P.query_start_loc[sq];
             pf_rows = (P.query_start_loc[sq + 1] - pf_q0) * P.gqa;
             pf_ctx = P.context_lens[sq];
-            if (rb * kMaxHeadsPerGroup >= pf_rows) return;   // no rows in this block (uniform)
-            pf_lmax = pf_ctx + (min(pf_rows, (rb + 1) * kMaxHeadsPerGroup) - 1) / P.gqa + 1;
+            if (rb * kPrefixRows >= pf_rows) return;   // no rows in this block (uniform)
+            pf_lmax = pf_ctx + (min(pf_rows, (rb + 1) * kPrefixRows) - 1) / P.gqa + 1;
             L = pf_lmax;
         } else {
             L = P.seq_lens[blockIdx.x / (KVH * HG)];
         }
         item = 0;
-        item_end = L > 0 ? (L + kPartition - 1) / kPartition : 0;
+        const int span = PREFIX ? kPrefixSlice : kPartition;
+        item_end = L > 0 ? (L + span - 1) / span : 0;
     } else if constexpr (COMPACT) {
         const int tid = tid0, lane = tid0 & 63, wv = tid0 >> 6;
         const int nthr = WAVES * 64;
@@ -275,7 +279,16 @@ phase1_kernel(const Phase1Params P) {
     // sum and the unnormalised output of the partitions merged so far.
     constexpr int VEC = QDT == F32 ? 4 : 8;
     constexpr int PER_HEAD = D / VEC;
-    constexpr int NRUN = SINGLE ? (kMaxHeadsPerGroup * PER_HEAD + WAVES * 64 - 1) / (WAVES * 64) : 1;
+    constexpr int NRUN = (SINGLE && !PREFIX) ? (kMaxHeadsPerGroup * PER_HEAD + WAVES * 64 - 1) / (WAVES * 64) : 1;
+    // P V accumulators (O^T tiles), the rounded-weight sums and the exact
+    // sums: per item, except in prefix attention, where they run over the
+    // whole key range together with the running max pf_m (per column).
+    f32x4 o[NDT];
+    f32x4 osum = {0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.0f;
+    float pf_m = -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float run_m[NRUN], run_l[NRUN], run_o[NRUN][VEC];
 #pragma unroll
     for (int k = 0; k < NRUN; ++k) {
@@ -292,7 +305,7 @@ phase1_kernel(const Phase1Params P) {
         hg = blockIdx.x % HG;
         g = (blockIdx.x / HG) % KVH;
         s = blockIdx.x / (HG * KVH);
-        p = item;
+        p = PREFIX ? item / (kPartition / kPrefixSlice) : item;
     } else if constexpr (COMPACT) {
         int r = item / HG;
         g = r % KVH;
@@ -327,7 +340,8 @@ phase1_kernel(const Phase1Params P) {
     const int L = PREFIX ? pf_lmax : P.seq_lens[s];
     const int start = p * kPartition;
     const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
-    const int nh = PREFIX ? min(kMaxHeadsPerGroup, pf_rows - hg * kMaxHeadsPerGroup)
+    const int rb0 = (hg * WAVES + wv) * kMaxHeadsPerGroup;   // prefix: this wavefront's first row
+    const int nh = PREFIX ? max(0, min(kMaxHeadsPerGroup, pf_rows - rb0))
                           : min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
 
     if (start >= L) {   // unused partition slot (dense and compact schedules)
@@ -355,7 +369,7 @@ phase1_kernel(const Phase1Params P) {
     const uint8_t *qrow;
     int lcol = L;   // prefix attention: this lane's column's causal limit (keys t < lcol)
     if constexpr (PREFIX) {
-        const int rr = hg * kMaxHeadsPerGroup + col;
+        const int rr = rb0 + col;
         const int j = rr / P.gqa;
         qrow = reinterpret_cast<const uint8_t *>(P.query) +
                (((int64_t)(pf_q0 + j) * P.num_heads + g * P.gqa + (rr - j * P.gqa)) * D) * QB;
@@ -364,7 +378,7 @@ phase1_kernel(const Phase1Params P) {
         qrow = reinterpret_cast<const uint8_t *>(P.query) + (((int64_t)s * P.num_heads + h0 + col) * D) * QB;
     }
     // the block's smallest column limit (its first row's): units below it need no mask
-    const int lmin = PREFIX ? pf_ctx + (hg * kMaxHeadsPerGroup) / P.gqa + 1 : L;
+    const int lmin = PREFIX ? (nh > 0 ? pf_ctx + rb0 / P.gqa + 1 : L) : L;
     Words<X * QB / 4> qw[NKL];
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
@@ -398,7 +412,10 @@ phase1_kernel(const Phase1Params P) {
     constexpr int UNIT = 32;
     constexpr int UPW = (kPartition / UNIT) / WAVES;       // units per wavefront
     const int nunits = (n_tok + UNIT - 1) / UNIT;
-    auto unit_of = [&](int u) { return wv + WAVES * u; };
+    auto unit_of = [&](int u) {
+        if constexpr (PREFIX) return (item % (kPartition / kPrefixSlice)) * UPW + u;
+        else return wv + WAVES * u;
+    };
     auto clamp_unit = [&](int t) { return t < nunits ? t : 0; };
 
     // Load groups: K of a unit in KG groups (halves when large), V of a unit in
@@ -508,9 +525,10 @@ phase1_kernel(const Phase1Params P) {
         return acc;
     };
 
-    f32x4 o[NDT];
+    if constexpr (!PREFIX) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     u32x4 kbuf[PF][KH][NKL];
     Words<VW> vbuf[PF][DPG];
@@ -579,7 +597,20 @@ phase1_kernel(const Phase1Params P) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, sc[u][e]);
     m = wave_max(m);
-    const float mu = (m == -INFINITY) ? 0.0f : m;
+    float mu = (m == -INFINITY) ? 0.0f : m;
+    if constexpr (PREFIX) {   // rescale the running state to the new running max
+        const float mn = fmaxf(pf_m, m);
+        const float fo = mn == -INFINITY ? 1.0f : exp2_fast(pf_m - mn);
+        pf_m = mn;
+        mu = mn == -INFINITY ? 0.0f : mn;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[dt][i] *= fo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) osum[i] *= fo;
+        lsum *= fo;
+    }
 
     // Pass 2: exp and P V.  lsum is the exact sum of the weights (stored as
     // exp_sums); lsum_r sums the weights as they enter the MFMAs, so that the
@@ -587,10 +618,11 @@ phase1_kernel(const Phase1Params P) {
     // carry P as hi + lo, two 16-bit parts (~16 significant bits).
     // The rounded weights' sum comes from one more MFMA pair per unit against
     // an all-ones A operand (every row of that tile is sum_t P[t][head]).
-    float lsum = 0.0f, lsum_r = 0.0f;
+    float lsum_r = 0.0f;
+    if constexpr (!PREFIX) lsum = 0.0f;
     float pr[8];
     u32x4 ph = {0u, 0u, 0u, 0u}, pl = {0u, 0u, 0u, 0u};
-    f32x4 osum = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!PREFIX) osum = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t one2 = pack2<QDT == F32 ? BF16 : QDT>(1.0f, 1.0f);
     const u32x4 ones = {one2, one2, one2, one2};
     // Raw-word masks zeroing V of tokens past the sequence end (word w of a
@@ -678,6 +710,7 @@ phase1_kernel(const Phase1Params P) {
         }
         issue(j + PF);
     }
+    if constexpr (PREFIX) continue;   // the running state stays in registers
     lsum = wave_sum_groups(lsum);
     if constexpr (S::kF32) lsum_r = lsum;
     else lsum_r = osum[0];
@@ -775,11 +808,37 @@ phase1_kernel(const Phase1Params P) {
         if constexpr (!COMPACT) break;
     }   // item loop
 
+    if constexpr (PREFIX) {   // each wavefront normalises and writes its own 16 rows
+        const int lane = tid0 & 63, wv = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+        const int col = lane & 15, grp = lane >> 4;
+        const int hg = blockIdx.x % HG, g = (blockIdx.x / HG) % KVH;
+        const int rb0 = (hg * WAVES + wv) * kMaxHeadsPerGroup;
+        float lr;
+        if constexpr (S::kF32) lr = wave_sum_groups(lsum);
+        else lr = osum[0];
+        if (col < pf_rows - rb0) {
+            const int rr = rb0 + col, j = rr / P.gqa;
+            const int64_t orow = (int64_t)(pf_q0 + j) * P.num_heads + g * P.gqa + (rr - j * P.gqa);
+            const float inv = lr > 0.0f ? P.v_scale / lr : 0.0f;
+            uint8_t *base = reinterpret_cast<uint8_t *>(P.tmp_out) + orow * D * QB;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const int d0 = 16 * dt + 4 * grp;   // this lane's 4 consecutive head-dim elements
+                if (d0 < D) {
+                    const float r0 = o[dt][0] * inv, r1 = o[dt][1] * inv, r2 = o[dt][2] * inv, r3 = o[dt][3] * inv;
+                    if constexpr (QDT == F32)
+                        *reinterpret_cast<f32x4 *>(base + d0 * QB) = f32x4{r0, r1, r2, r3};
+                    else
+                        *reinterpret_cast<u32x2 *>(base + d0 * QB) = u32x2{pack2<QDT>(r0, r1), pack2<QDT>(r2, r3)};
+                }
+            }
+        }
+        return;
+    }
     if constexpr (SINGLE) {   // the normalised output, written once (zero rows for an empty sequence)
         const int hg = blockIdx.x % HG, g = (blockIdx.x / HG) % KVH, s = blockIdx.x / (HG * KVH);
         const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
-        const int nh = PREFIX ? min(kMaxHeadsPerGroup, pf_rows - hg * kMaxHeadsPerGroup)
-                              : min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
+        const int nh = min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
 #pragma unroll
         for (int k = 0; k < NRUN; ++k) {
             const int idx = tid0 + k * WAVES * 64;
@@ -790,12 +849,7 @@ phase1_kernel(const Phase1Params P) {
                 float r[VEC];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) r[e] = run_o[k][e] * inv;
-                int64_t orow = (int64_t)s * P.num_heads + h0 + hh;   // output row (token, head)
-                if constexpr (PREFIX) {
-                    const int rr = hg * kMaxHeadsPerGroup + hh;
-                    const int j = rr / P.gqa;
-                    orow = (int64_t)(pf_q0 + j) * P.num_heads + g * P.gqa + (rr - j * P.gqa);
-                }
+                const int64_t orow = (int64_t)s * P.num_heads + h0 + hh;   // output row (sequence, head)
                 uint8_t *dst = reinterpret_cast<uint8_t *>(P.tmp_out) + (orow * D + d0) * QB;
                 if constexpr (QDT == F32) {
                     *reinterpret_cast<f32x4 *>(dst) = f32x4{r[0], r[1], r[2], r[3]};
