@@ -117,3 +117,37 @@ def test_prefix_rejects_fp8_cache():
     with pytest.raises(ValueError):
         pav2.paged_prefix_attention(torch.empty_like(pw.query), pw.query, kc, pw.value_cache, pw.block_tables,
                                     pw.query_start_loc, pw.context_lens, 2, 6)
+
+
+def test_prefix_full_size_sampled():
+    """The benchmark's chunked prefill (4 x (16384 cached + 512 new) tokens, H = 24,
+    kv_h = 4, d = 256, bf16), launched as bench.py launches it; sampled rows
+    against the oracle.  Row j of a chunk only sees keys up to ctx + j, so it
+    is checked as a one-token chunk over the written cache's first ctx + j
+    tokens, with the token's own key and value from the input tensors."""
+    import bench
+    c = bench.PREFIX_CASE
+    print("case prefix full size", flush=True)
+    pw = W.prefix_workload(c["ctx"], c["ql"], c["H"], c["KVH"], c["d"], c["bs"], dtype=c["dtype"], seed=c["seed"],
+                           device=DEV)
+    pav2.reshape_and_cache(pw.key, pw.value, pw.key_cache, pw.value_cache, pw.slot_mapping)
+    out = torch.full_like(pw.query, float("nan"))
+    max_seq = max(a + b for a, b in zip(c["ctx"], c["ql"]))
+    pav2.paged_prefix_attention(out, pw.query, pw.key_cache, pw.value_cache, pw.block_tables, pw.query_start_loc,
+                                pw.context_lens, max(c["ql"]), max_seq)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    host = pw.to("cpu")
+    got = out.cpu()
+    qsl = host.query_start_loc
+    worst = 0.0
+    for s, j in [(0, 0), (0, 511), (1, 255), (2, 1), (3, 400), (3, 511)]:
+        q = int(qsl[s]) + j
+        ref = oracle.prefix_attention(host.query[q:q + 1], host.key[q:q + 1], host.value[q:q + 1], host.key_cache,
+                                      host.value_cache, host.block_tables[s:s + 1],
+                                      torch.tensor([0, 1], dtype=torch.int32),
+                                      torch.tensor([c["ctx"][s] + j], dtype=torch.int32), num_kv_heads=c["KVH"],
+                                      block_size=c["bs"], scale=c["d"] ** -0.5, q_dtype=oracle.BF16,
+                                      kv_dtype=oracle.BF16)
+        worst = max(worst, assert_close(got[q:q + 1], ref, "bf16"))
+    print(f"  worst {worst:.3g}", flush=True)
