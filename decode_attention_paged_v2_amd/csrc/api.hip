@@ -419,9 +419,8 @@ int pav2_paged_prefix_attention(void *output, const void *query, const void *key
     p.blk_stride = p.head_stride * num_kv_heads;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.v_scale = 1.0f;
-    // 16 rows per wavefront, no partition-count prefix
-    const int lds = pav2::phase1_lds_bytes(pav2::kMaxHeadsPerGroup, head_size, pav2::kPhase1Waves, p.bs_log2,
-                                           num_seqs, false);
+    // no cross-wavefront partial outputs and no partition-count prefix
+    const int lds = pav2::phase1_lds_bytes(0, head_size, pav2::kPhase1Waves, p.bs_log2, num_seqs, false);
     return launch_status(pav2::launch_phase1(p, (int)dtype, (int)dtype, head_size, pav2::kPhase1Waves, lds,
                                              static_cast<hipStream_t>(stream)),
                          "prefix attention");

@@ -7,12 +7,11 @@
 //   key_cache  [blk, g, i / x, off, i % x] = enc(key  [t, g, i] / k_scale)
 //   value_cache[blk, g, i,     off]        = enc(value[t, g, i] / v_scale)
 //
-// with x = 16 / element size of the cache dtype.  The quotient is an IEEE
-// float32 division (computed exactly as such, see quotient()); enc rounds to
-// the cache dtype to nearest, ties to even
-// (e4m3 after saturating to +-448, so no value overflows to NaN).  With unit
-// scales and a cache of the input's dtype the write is a plain copy.  Slots
-// < 0, or past the pool, write nothing.
+// with x = 16 / element size of the cache dtype.  The quotient is the IEEE
+// float32 quotient (see quotient()); enc rounds it to the cache dtype to
+// nearest, ties to even (e4m3 after saturating to +-448, so no value
+// overflows to NaN).  With unit scales and a cache of the input's dtype the
+// write is a plain copy.  Slots < 0, or past the pool, write nothing.
 //
 // One workgroup per (tile of consecutive tokens, kv head): 16 tokens, or 32
 // for one-byte caches so that a prefill tile fills whole 32-byte value rows
@@ -28,10 +27,10 @@
 //   conflict in LDS banks);
 // * stores: keys token-fastest (tokens with consecutive slots give
 //   block_size * 16 contiguous bytes per chunk); values as 8 tokens of one
-//   head-dim row per lane (gathered from the 8 token rows in LDS), one vector
-//   store when their slots are 8
-//   consecutive, 8-aligned positions (always within one block, as block
-//   sizes are powers of two >= 8), else element by element.
+//   head-dim row per lane (gathered from the 8 token rows in LDS), one
+//   vector store when their slots are 8 consecutive, 8-aligned positions
+//   (always within one block, as block sizes are powers of two >= 8), else
+//   element by element.
 #include "cache.h"
 
 namespace pav2 {

@@ -177,7 +177,8 @@ phase1_kernel(const Phase1Params P) {
     const int maxP = P.max_num_partitions;
     const int HG = P.head_groups;
     const int KVH = P.num_kv_heads;
-    const int heads_alloc = PREFIX ? kMaxHeadsPerGroup : min(P.gqa, kMaxHeadsPerGroup);
+    // (prefix attention merges nothing across wavefronts: no partial-output area)
+    const int heads_alloc = PREFIX ? 0 : min(P.gqa, kMaxHeadsPerGroup);
     constexpr int kBsLog2 = BS == 16 ? 4 : (BS == 32 ? 5 : -1);
     const int bs_log2 = kBsLog2 >= 0 ? kBsLog2 : P.bs_log2;
     const int bs_mask = (1 << bs_log2) - 1;
