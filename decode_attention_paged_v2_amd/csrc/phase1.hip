@@ -207,12 +207,17 @@ phase1_kernel(const Phase1Params P) {
     // rows) up to the block's last row's limit context + j + 1, each keeping
     // its rows' running (max, sum, output) in registers.
     int pf_q0 = 0, pf_ctx = 0, pf_rows = 0, pf_lmax = 0;
+    // Single pass and prefix: the workgroup's (sequence, kv head, group)
+    // index.  Prefix attention numbers its workgroups XCD by XCD (the grid is
+    // a multiple of 8, blockIdx % 8 picks the XCD), so the row blocks of one
+    // (sequence, kv head), which stream the same keys, share one L2.
+    const int wg = PREFIX ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
     int item, item_end;
     if constexpr (SINGLE) {
-        if ((int)blockIdx.x >= P.num_work) return;
+        if (wg >= P.num_work) return;
         int L;
         if constexpr (PREFIX) {
-            const int sq = blockIdx.x / (KVH * HG), rb = blockIdx.x % HG;
+            const int sq = wg / (KVH * HG), rb = wg % HG;
             pf_q0 = P.query_start_loc[sq];
             pf_rows = (P.query_start_loc[sq + 1] - pf_q0) * P.gqa;
             pf_ctx = P.context_lens[sq];
@@ -220,7 +225,7 @@ phase1_kernel(const Phase1Params P) {
             pf_lmax = pf_ctx + (min(pf_rows, (rb + 1) * kPrefixRows) - 1) / P.gqa + 1;
             L = pf_lmax;
         } else {
-            L = P.seq_lens[blockIdx.x / (KVH * HG)];
+            L = P.seq_lens[wg / (KVH * HG)];
         }
         item = 0;
         const int span = PREFIX ? kPrefixSlice : kPartition;
@@ -303,9 +308,9 @@ phase1_kernel(const Phase1Params P) {
     int hg = item % HG;
     int s, g, p;
     if constexpr (SINGLE) {
-        hg = blockIdx.x % HG;
-        g = (blockIdx.x / HG) % KVH;
-        s = blockIdx.x / (HG * KVH);
+        hg = wg % HG;
+        g = (wg / HG) % KVH;
+        s = wg / (HG * KVH);
         p = PREFIX ? item / (kPartition / kPrefixSlice) : item;
     } else if constexpr (COMPACT) {
         int r = item / HG;
@@ -812,7 +817,7 @@ phase1_kernel(const Phase1Params P) {
     if constexpr (PREFIX) {   // each wavefront normalises and writes its own 16 rows
         const int lane = tid0 & 63, wv = __builtin_amdgcn_readfirstlane(tid0 >> 6);
         const int col = lane & 15, grp = lane >> 4;
-        const int hg = blockIdx.x % HG, g = (blockIdx.x / HG) % KVH;
+        const int hg = wg % HG, g = (wg / HG) % KVH;
         const int rb0 = (hg * WAVES + wv) * kMaxHeadsPerGroup;
         float lr;
         if constexpr (S::kF32) lr = wave_sum_groups(lsum);
@@ -837,7 +842,7 @@ phase1_kernel(const Phase1Params P) {
         return;
     }
     if constexpr (SINGLE) {   // the normalised output, written once (zero rows for an empty sequence)
-        const int hg = blockIdx.x % HG, g = (blockIdx.x / HG) % KVH, s = blockIdx.x / (HG * KVH);
+        const int hg = wg % HG, g = (wg / HG) % KVH, s = wg / (HG * KVH);
         const int h0 = g * P.gqa + hg * kMaxHeadsPerGroup;
         const int nh = min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
 #pragma unroll
@@ -906,8 +911,10 @@ hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
             per_cu = 1;
         const int cap = kPhase1CompactRounds * device_cu_count() * per_cu;
         grid = grid < cap ? grid : cap;
-    } else if (SCHED >= 2) {
-        grid = p.num_work;   // one workgroup per (sequence, kv head, head or row group)
+    } else if (SCHED == 2) {
+        grid = p.num_work;   // one workgroup per (sequence, kv head, head group)
+    } else if (SCHED == 3) {
+        grid = (p.num_work + 7) / 8 * 8;   // one per (sequence, kv head, row block), a multiple of 8
     }
     hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, SCHED, BS>), dim3(grid), dim3(WAVES * 64), lds,
                        stream, p);
