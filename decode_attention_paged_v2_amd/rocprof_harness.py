@@ -1,7 +1,7 @@
 """rocprofv3 harness: per-kernel durations and HBM traffic of the decode path.
 
     python -m decode_attention_paged_v2_amd.rocprof_harness --config long_gqa \
-        --out gpurun_out/prof [--pmc] [--sq]
+        --out gpurun_out/prof [--pmc] [--sq] [--entry v1]
 
 Runs `bench.py` (a few steps, no CPU baseline) under
 
@@ -12,9 +12,11 @@ Runs `bench.py` (a few steps, no CPU baseline) under
   1 GiB copy).  Each counter is scaled by the ratio of the copy's known bytes
   to what the counter reports for it, giving HBM bytes per phase-1 launch;
 * with `--sq`, two passes of SQ instruction counters over phase 1, reported
-  per (work item, wavefront).
+  per (work item, wavefront);
+* with `--entry v1`, the same over the single-pass entry point (one launch
+  per step, priced with that entry point's algorithmic bytes).
 
-Writes `<out>/<kernel>_<config>.md` (a short summary with the commands) and
+Writes `<out>/<kernel>_<config>.md` (`phase1_`, or `v1_` for the single pass) (a short summary with the commands) and
 `<out>/<kernel>_<config>.json` (the numbers, plus a hash of the kernel sources
 so that bench.py can tell whether the counters still describe the current
 kernel).  rocprofv3 runs as a child process from /tmp with TMPDIR=/tmp; this
@@ -86,21 +88,25 @@ def _kind(name: str) -> str:
     return "other"
 
 
-def _bench_args(config: str, mode: str, steps: int, warmup: int) -> list:
+def _bench_args(config: str, mode: str, steps: int, warmup: int, entry: str = "v2") -> list:
     args = [sys.executable, BENCH, "--config", config, "--steps", str(steps), "--warmup", str(warmup),
             "--no-cpu-baseline"]
     if mode in ("cache_write", "prefix"):
         return args + ["--mode", mode]
-    return args + ["--flush-steps", "0"]
+    return args + ["--flush-steps", "0"] + (["--entry", "v1"] if entry == "v1" else [])
 
 
-def kernel_trace(config: str, out: str, steps: int = 10, mode: str = "decode") -> dict:
-    d = os.path.join(out, f"trace_{mode}_{config}")
+def _tag(mode: str, config: str, entry: str) -> str:
+    return f"{mode}_{config}" if entry == "v2" else f"{mode}_v1_{config}"
+
+
+def kernel_trace(config: str, out: str, steps: int = 10, mode: str = "decode", entry: str = "v2") -> dict:
+    d = os.path.join(out, "trace_" + _tag(mode, config, entry))
     shutil.rmtree(d, ignore_errors=True)
-    bench = _bench_args(config, mode, steps, 2)
+    bench = _bench_args(config, mode, steps, 2, entry)
     cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", d, "-o", "run", "--output-format", "csv",
            "--"] + bench
-    _run(cmd, os.path.join(out, f"trace_{mode}_{config}.log"), 300)
+    _run(cmd, d + ".log", 300)
     rel = os.path.relpath(d, ROOT)
     res = {"command": " ".join(["rocprofv3", "--kernel-trace", "--stats", "-d", rel, "-o", "run",
                                 "--output-format", "csv", "--", "python3", "bench.py"] + bench[2:])}
@@ -124,18 +130,19 @@ def kernel_trace(config: str, out: str, steps: int = 10, mode: str = "decode") -
     return res
 
 
-def pmc(config: str, out: str, mode: str = "decode") -> dict:
+def pmc(config: str, out: str, mode: str = "decode", entry: str = "v2") -> dict:
     """FETCH_SIZE and WRITE_SIZE per launch of the profiled kernels, scaled by the copy reference."""
     res = {}
-    kinds = ("phase1", "phase2") if mode == "decode" else ("cache_write",)
+    # the single-pass entry point launches the phase-1 kernel template only
+    kinds = ("cache_write",) if mode != "decode" else ("phase1",) if entry == "v1" else ("phase1", "phase2")
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         for what in (config, "copy"):
-            d = os.path.join(out, f"pmc_{counter}_{what if what == 'copy' else mode + '_' + what}")
+            d = os.path.join(out, f"pmc_{counter}_" + ("copy" if what == "copy" else _tag(mode, what, entry)))
             shutil.rmtree(d, ignore_errors=True)
             if what == "copy":
                 bench = [sys.executable, BENCH, "--mode", "copy", "--steps", "3", "--warmup", "1"]
             else:
-                bench = _bench_args(what, mode, 3, 1)
+                bench = _bench_args(what, mode, 3, 1, entry)
             cmd = ["rocprofv3", "--pmc", counter, "-d", d, "-o", "run", "--output-format", "csv",
                    "--"] + bench
             _run(cmd, d + ".log", 120)
@@ -203,15 +210,23 @@ def algorithmic_bytes(config: str) -> dict:
     return accounting.spec_bytes(workloads.SPECS[config])
 
 
-def write_summary(config: str, out: str, trace: dict, counters: dict | None, sqv: dict | None = None) -> str:
-    alg = algorithmic_bytes(config)
+def write_summary(config: str, out: str, trace: dict, counters: dict | None, sqv: dict | None = None,
+                  entry: str = "v2") -> str:
+    alg = dict(algorithmic_bytes(config))
+    if entry == "v1":
+        # the single pass reads what phase 1 reads and writes the final rows only
+        alg["phase1"] = alg["v1"]
+        alg["phase1_write"] = alg["v1"] - alg["phase1_read"]
     p1 = trace["phase1"]
-    name = "phase1_" + config
-    lines = [f"# Phase 1 / phase 2 profile: {config}", "",
+    name = ("phase1_" if entry == "v2" else "v1_") + config
+    title = "Phase 1 / phase 2" if entry == "v2" else "Single-pass (V1)"
+    label = "Phase-1" if entry == "v2" else "Single-pass"
+    lines = [f"# {title} profile: {config}", "",
              f"Kernel sources hash: `{source_hash()}`", "",
              "Kernel trace command (from the repository root):", "",
              "    python -m decode_attention_paged_v2_amd.rocprof_harness --config "
-             f"{config} --out gpurun_out/prof{' --pmc' if counters else ''}{' --sq' if sqv else ''}", "",
+             f"{config}{' --entry v1' if entry == 'v1' else ''} --out gpurun_out/prof"
+             f"{' --pmc' if counters else ''}{' --sq' if sqv else ''}", "",
              "which runs:", "", "    " + trace["command"], "",
              "| kernel | calls | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|"]
     for k in ("phase1", "phase2"):
@@ -220,10 +235,10 @@ def write_summary(config: str, out: str, trace: dict, counters: dict | None, sqv
             lines.append(f"| `{t['name'][:90]}` | {t['calls']} | {t['avg_us']:.2f} | {t['min_us']:.2f} | "
                          f"{t['max_us']:.2f} |")
     gbps = alg["phase1"] / (p1["avg_us"] * 1e-6) / 1e9
-    lines += ["", f"Phase-1 algorithmic bytes per launch: {alg['phase1']:,} "
+    lines += ["", f"{label} algorithmic bytes per launch: {alg['phase1']:,} "
                   f"(K/V {alg['kv']:,}); at the average duration that is {gbps:.1f} GB/s = "
                   f"{100 * gbps / 8000:.1f} % of 8 TB/s."]
-    data = {"config": config, "source_hash": source_hash(), "trace": trace, "algorithmic": alg,
+    data = {"config": config, "entry": entry, "source_hash": source_hash(), "trace": trace, "algorithmic": alg,
             "phase1_achieved_GBps": gbps, "taken": time.strftime("%Y-%m-%d %H:%M:%S")}
     if counters:
         f1, w1 = counters["phase1_fetch_bytes"], counters["phase1_write_bytes"]
@@ -236,10 +251,10 @@ def write_summary(config: str, out: str, trace: dict, counters: dict | None, sqv
                   f"| WRITE_SIZE of the 1 GiB copy (KiB) | {counters['WRITE_SIZE_copy_kib']:.1f} |",
                   f"| scale factors (known / counted) | fetch {counters['FETCH_SIZE_scale']:.4f}, "
                   f"write {counters['WRITE_SIZE_scale']:.4f} |",
-                  f"| phase-1 FETCH_SIZE per launch (KiB, raw) | {counters['FETCH_SIZE_phase1_kib']:.1f} |",
-                  f"| phase-1 WRITE_SIZE per launch (KiB, raw) | {counters['WRITE_SIZE_phase1_kib']:.1f} |",
-                  f"| phase-1 HBM read bytes (scaled) | {f1:,.0f} |",
-                  f"| phase-1 HBM write bytes (scaled) | {w1:,.0f} |",
+                  f"| {label} FETCH_SIZE per launch (KiB, raw) | {counters['FETCH_SIZE_phase1_kib']:.1f} |",
+                  f"| {label} WRITE_SIZE per launch (KiB, raw) | {counters['WRITE_SIZE_phase1_kib']:.1f} |",
+                  f"| {label} HBM read bytes (scaled) | {f1:,.0f} |",
+                  f"| {label} HBM write bytes (scaled) | {w1:,.0f} |",
                   f"| algorithmic reads / writes | {alg['phase1_read']:,} / {alg['phase1_write']:,} |",
                   f"| measured / algorithmic | reads {f1 / alg['phase1_read']:.4f}, "
                   f"writes {w1 / alg['phase1_write']:.4f} |"]
@@ -348,20 +363,22 @@ def main():
     ap.add_argument("--pmc", action="store_true", help="HBM FETCH_SIZE / WRITE_SIZE passes")
     ap.add_argument("--sq", action="store_true", help="instruction-mix / utilisation passes")
     ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--entry", default="v2", choices=["v2", "v1"],
+                    help="decode mode: v2 (both phases) or v1 (the single-pass entry point)")
     a = ap.parse_args()
     out = os.path.abspath(a.out)
     os.makedirs(out, exist_ok=True)
-    trace = kernel_trace(a.config, out, a.steps, a.mode)
+    trace = kernel_trace(a.config, out, a.steps, a.mode, a.entry)
     if a.mode == "prefix":
         path = write_prefix_summary(out, trace)
         print(open(path).read(), flush=True)
         return
-    counters = pmc(a.config, out, a.mode) if a.pmc else None
+    counters = pmc(a.config, out, a.mode, a.entry) if a.pmc else None
     if a.mode == "cache_write":
         path = write_cache_summary(a.config, out, trace, counters)
     else:
         sqv = sq(a.config, out) if a.sq else None
-        path = write_summary(a.config, out, trace, counters, sqv)
+        path = write_summary(a.config, out, trace, counters, sqv, a.entry)
     print(open(path).read(), flush=True)
 
 
