@@ -204,6 +204,21 @@ def prefix_flops(ctx, ql, H, d):
     return sum(4 * d * H * (q * c + q * (q + 1) // 2) for c, q in zip(ctx, ql))
 
 
+def measured_prefix_traffic():
+    """HBM bytes per prefix-attention launch (scaled FETCH_SIZE + WRITE_SIZE)
+    from the committed summary, or None when there is none or it was taken on
+    different kernel sources."""
+    from decode_attention_paged_v2_amd import rocprof_harness
+    path = os.path.join(ROOT, "profiles", "prefix_attention.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    if data.get("source_hash") != rocprof_harness.source_hash() or "traffic_bytes" not in data:
+        return None
+    return round(float(data["traffic_bytes"]))
+
+
 def prefix_bench(args, dev):
     """Paged prefix attention over a chunked prefill (the chunk's keys and
     values written into the cache first, outside the timed region)."""
@@ -232,7 +247,8 @@ def prefix_bench(args, dev):
         "ms_min": round(mn, 5), "wall_ms_per_launch": round(wall, 5),
         "kv_GBps_if_read_once": round(kv_bytes / (mean * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_prefix_traffic(),
                      "kernel": "phase1_kernel (prefix)", "algorithmic_flops_per_launch": flops},
         "library": pav2.lib_path(),
     }

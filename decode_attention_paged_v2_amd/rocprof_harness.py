@@ -97,6 +97,8 @@ def _bench_args(config: str, mode: str, steps: int, warmup: int, entry: str = "v
 
 
 def _tag(mode: str, config: str, entry: str) -> str:
+    if mode == "prefix":   # one fixed case, no --config
+        return mode
     return f"{mode}_{config}" if entry == "v2" else f"{mode}_v1_{config}"
 
 
@@ -134,7 +136,8 @@ def pmc(config: str, out: str, mode: str = "decode", entry: str = "v2") -> dict:
     """FETCH_SIZE and WRITE_SIZE per launch of the profiled kernels, scaled by the copy reference."""
     res = {}
     # the single-pass entry point launches the phase-1 kernel template only
-    kinds = ("cache_write",) if mode != "decode" else ("phase1",) if entry == "v1" else ("phase1", "phase2")
+    kinds = {"cache_write": ("cache_write",), "prefix": ("phase1",)}.get(
+        mode, ("phase1",) if entry == "v1" else ("phase1", "phase2"))
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         for what in (config, "copy"):
             d = os.path.join(out, f"pmc_{counter}_" + ("copy" if what == "copy" else _tag(mode, what, entry)))
@@ -327,7 +330,7 @@ def write_cache_summary(config: str, out: str, trace: dict, counters: dict | Non
     return os.path.join(out, name + ".md")
 
 
-def write_prefix_summary(out: str, trace: dict) -> str:
+def write_prefix_summary(out: str, trace: dict, counters: dict | None = None) -> str:
     import importlib.util
     spec = importlib.util.spec_from_file_location("bench_for_counts", BENCH)
     bench = importlib.util.module_from_spec(spec)
@@ -340,7 +343,8 @@ def write_prefix_summary(out: str, trace: dict) -> str:
     lines = ["# Paged prefix attention profile: 4 seqs x (16384 cached + 512 new tokens), H=24, kv_h=4, d=256, bf16",
              "", f"Kernel sources hash: `{source_hash('decode')}`", "",
              "Command (from the repository root):", "",
-             "    python -m decode_attention_paged_v2_amd.rocprof_harness --mode prefix --out gpurun_out/prof", "",
+             "    python -m decode_attention_paged_v2_amd.rocprof_harness --mode prefix --out gpurun_out/prof"
+             + (" --pmc" if counters else ""), "",
              "which runs:", "", "    " + trace["command"], "",
              "| kernel | calls | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|",
              f"| `{t['name'][:90]}` | {t['calls']} | {t['avg_us']:.2f} | {t['min_us']:.2f} | {t['max_us']:.2f} |", "",
@@ -348,6 +352,29 @@ def write_prefix_summary(out: str, trace: dict) -> str:
              f"that is {tf:.1f} TFLOP/s = {100 * tf / 2500:.2f} % of the 2.5 PFLOP/s bf16 MFMA peak."]
     data = {"source_hash": source_hash("decode"), "trace": trace, "algorithmic_flops": flops, "achieved_TFLOPs": tf,
             "taken": time.strftime("%Y-%m-%d %H:%M:%S")}
+    if counters:
+        # unique bytes: every (cached + new) token's K and V once, the queries,
+        # the block-table rows and per-sequence metadata; writes: the output rows
+        eb = 4 if c["dtype"] == "f32" else 2
+        rows = sum(c["ql"]) * c["H"] * c["d"] * eb
+        tokens = sum(a + b for a, b in zip(c["ctx"], c["ql"]))
+        blocks = sum(-(-(a + b) // c["bs"]) for a, b in zip(c["ctx"], c["ql"]))
+        alg_r = tokens * c["KVH"] * 2 * c["d"] * eb + rows + 4 * blocks + 3 * 4 * len(c["ql"])
+        f, w = counters["phase1_fetch_bytes"], counters["phase1_write_bytes"]
+        data["counters"] = counters
+        data["traffic_bytes"] = f + w
+        data["unique_read_bytes"], data["unique_write_bytes"] = alg_r, rows
+        lines += ["", "HBM counters (`rocprofv3 --pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, over the same bench "
+                      "command and over `bench.py --mode copy`, a 1 GiB copy; prefix-kernel dispatches only):", "",
+                  "| quantity | value |", "|---|---|",
+                  f"| scale factors (known / counted) | fetch {counters['FETCH_SIZE_scale']:.4f}, "
+                  f"write {counters['WRITE_SIZE_scale']:.4f} |",
+                  f"| FETCH_SIZE / WRITE_SIZE per launch (KiB, raw) | {counters['FETCH_SIZE_phase1_kib']:.1f} / "
+                  f"{counters['WRITE_SIZE_phase1_kib']:.1f} |",
+                  f"| HBM read / write bytes (scaled) | {f:,.0f} / {w:,.0f} |",
+                  f"| unique reads (K/V of every token once, queries, tables) / writes (output) | "
+                  f"{alg_r:,} / {rows:,} |",
+                  f"| measured / unique | reads {f / alg_r:.4f}, writes {w / rows:.4f} |"]
     with open(os.path.join(out, name + ".md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     with open(os.path.join(out, name + ".json"), "w") as fh:
@@ -370,7 +397,7 @@ def main():
     os.makedirs(out, exist_ok=True)
     trace = kernel_trace(a.config, out, a.steps, a.mode, a.entry)
     if a.mode == "prefix":
-        path = write_prefix_summary(out, trace)
+        path = write_prefix_summary(out, trace, pmc(a.config, out, a.mode) if a.pmc else None)
         print(open(path).read(), flush=True)
         return
     counters = pmc(a.config, out, a.mode, a.entry) if a.pmc else None
