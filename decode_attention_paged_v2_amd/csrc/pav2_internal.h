@@ -93,10 +93,18 @@ hipError_t launch_check_inputs(const int32_t *block_tables, const int32_t *seq_l
 #define PAV2_PHASE1_NONTEMPORAL 1
 #endif
 constexpr int kPhase1Waves = PAV2_PHASE1_WAVES;
+#ifndef PAV2_PREFIX_SLICE
+#define PAV2_PREFIX_SLICE 512
+#endif
 // Prefix attention: rows (query token, head) per workgroup, 16 per
-// wavefront, and the key slice all wavefronts take per step (their 4 units).
+// wavefront, and the key slice every wavefront walks per step (32-token
+// units; a divisor of the partition).  A whole partition per step halves
+// the per-step max reduction and rescale against 256 tokens and keeps more
+// loads in flight; the bf16 d = 256 kernel then holds about 400 registers
+// (one wavefront per SIMD, no spills).
 constexpr int kPrefixRows = kPhase1Waves * kMaxHeadsPerGroup;
-constexpr int kPrefixSlice = kPartition / kPhase1Waves;
+constexpr int kPrefixSlice = PAV2_PREFIX_SLICE;
+static_assert(kPrefixSlice % 32 == 0 && kPartition % kPrefixSlice == 0, "prefix slice: 32-token units dividing the partition");
 constexpr int kPhase1Occupancy = PAV2_PHASE1_OCCUPANCY;
 constexpr bool kPhase1NonTemporal = PAV2_PHASE1_NONTEMPORAL != 0;
 constexpr int kPhase2Threads = 256;

@@ -416,7 +416,7 @@ phase1_kernel(const Phase1Params P) {
     // round-robin; a unit past the end is clamped to unit 0 (its tokens are
     // then all masked).
     constexpr int UNIT = 32;
-    constexpr int UPW = (kPartition / UNIT) / WAVES;       // units per wavefront
+    constexpr int UPW = PREFIX ? kPrefixSlice / UNIT : (kPartition / UNIT) / WAVES;   // units per wavefront
     const int nunits = (n_tok + UNIT - 1) / UNIT;
     auto unit_of = [&](int u) {
         if constexpr (PREFIX) return (item % (kPartition / kPrefixSlice)) * UPW + u;
