@@ -16,8 +16,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpav2.so")
-SOURCES = ["api.hip", "phase1.hip", "phase2.hip", "check.hip", "cache.hip"]
-HEADERS = [os.path.join(CSRC, "pav2_internal.h"), os.path.join(CSRC, "cache.h"), os.path.join(ROOT, "include", "pav2.h")]
+# phase 1's kernel variants are split by (query dtype, cache dtype) pair so they compile in parallel
+PHASE1_PAIRS = ["f32_f32", "f16_f16", "bf16_bf16", "f32_fp8", "f16_fp8", "bf16_fp8"]
+SOURCES = (["api.hip", "phase1.hip"] + [f"phase1_{p}.hip" for p in PHASE1_PAIRS] +
+           ["phase2.hip", "check.hip", "cache.hip"])
+HEADERS = [os.path.join(CSRC, h) for h in ("pav2_internal.h", "phase1_kernel.h", "cache.h")] + \
+    [os.path.join(ROOT, "include", "pav2.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -41,7 +45,7 @@ def _compile(src: str, extra=(), build_dir: str = BUILD) -> str:
 def build(verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUILD) -> str:
     """Compile and link; ``extra`` adds hipcc flags (e.g. -DPAV2_PHASE1_WAVES=8)."""
     os.makedirs(build_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), max(1, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
     tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

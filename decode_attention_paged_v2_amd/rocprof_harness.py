@@ -38,9 +38,13 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 BENCH = os.path.join(ROOT, "bench.py")
+# What a summary's counters depend on: the kernels, and the launch plan in the
+# C ABI (schedule choice, grid sizes, LDS bytes, scale folding).
+_PLAN = [os.path.join(HERE, "csrc", "api.hip"), os.path.join(ROOT, "include", "pav2.h")]
 KERNEL_SOURCES = {
-    "decode": [os.path.join(HERE, "csrc", f) for f in ("phase1.hip", "phase2.hip", "pav2_internal.h")],
-    "cache_write": [os.path.join(HERE, "csrc", f) for f in ("cache.hip", "cache.h", "pav2_internal.h")],
+    "decode": sorted(glob.glob(os.path.join(HERE, "csrc", "phase1*"))) +
+              [os.path.join(HERE, "csrc", f) for f in ("phase2.hip", "pav2_internal.h")] + _PLAN,
+    "cache_write": [os.path.join(HERE, "csrc", f) for f in ("cache.hip", "cache.h", "pav2_internal.h")] + _PLAN,
 }
 
 

@@ -227,7 +227,7 @@ int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype
  * max_query_len >= every chunk's length and max_seq_len >= every context +
  * chunk length (host values sizing the grid and validating the table width).
  * One workgroup per (sequence, kv head, 64 (token, head) rows): its four
- * wavefronts hold 16 rows each and walk the same 128-token key slices up to
+ * wavefronts hold 16 rows each and walk the same 512-token key slices up to
  * their rows' causal limits with a running softmax.
  * No ALiBi or sliding window (the page's fallback applies neither).
  */

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import _tol
 import decode_attention_paged_v2_amd as pav2
 from decode_attention_paged_v2_amd import workloads as W
 
@@ -22,7 +23,6 @@ DEV = "cuda"
 _CODE = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}
 _TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 TOL = {"f32": 2e-5, "f16": 2e-3, "bf16": 2e-3}
-MANT = {"f32": 23, "f16": 10, "bf16": 7}
 
 
 def run_case(ctx, ql, H, KVH, d, BS, dtype, seed=0):
@@ -42,15 +42,9 @@ def run_case(ctx, ql, H, KVH, d, BS, dtype, seed=0):
 
 
 def assert_close(out, ref, dtype):
-    r = torch.from_numpy(ref).to(_TD[dtype]).double().numpy()     # the reference rounded to the output dtype
     got = out.double().numpy()
     assert np.isfinite(got).all()
-    a = np.maximum(np.abs(r), 2.0 ** -126)
-    allowed = np.maximum(TOL[dtype], 2.0 ** (np.floor(np.log2(a)) - MANT[dtype]))
-    err = np.abs(got - r)
-    worst = np.max(err - allowed)
-    assert worst <= 0, f"max error {err.max():.3g} beyond tolerance"
-    return float(err.max())
+    return _tol.check(got, ref, _TD[dtype], TOL[dtype], "prefix out")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -123,13 +117,17 @@ def test_prefix_full_size_sampled():
     """The benchmark's chunked prefill (4 x (16384 cached + 512 new) tokens, H = 24,
     kv_h = 4, d = 256, bf16), launched as bench.py launches it; sampled rows
     against the oracle.  Row j of a chunk only sees keys up to ctx + j, so it
-    is checked as a one-token chunk over the written cache's first ctx + j
-    tokens, with the token's own key and value from the input tensors."""
+    is checked as a one-token chunk over the first ctx + j cached tokens, with
+    the token's own key and value from the input tensors.  The oracle's cache
+    is the generator's starting cache with the chunks written into it by the
+    oracle's own cache write (from the key / value tensors): nothing the
+    oracle reads comes from the device's cache write."""
     import bench
     c = bench.PREFIX_CASE
     print("case prefix full size", flush=True)
     pw = W.prefix_workload(c["ctx"], c["ql"], c["H"], c["KVH"], c["d"], c["bs"], dtype=c["dtype"], seed=c["seed"],
                            device=DEV)
+    host = pw.to("cpu")   # the generator's inputs, taken before the device cache write
     pav2.reshape_and_cache(pw.key, pw.value, pw.key_cache, pw.value_cache, pw.slot_mapping)
     out = torch.full_like(pw.query, float("nan"))
     max_seq = max(a + b for a, b in zip(c["ctx"], c["ql"]))
@@ -137,15 +135,17 @@ def test_prefix_full_size_sampled():
                                 pw.context_lens, max(c["ql"]), max_seq)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    host = pw.to("cpu")
     got = out.cpu()
+    kb, vb = oracle.reshape_and_cache(host.key, host.value, host.key_cache, host.value_cache, host.slot_mapping,
+                                      block_size=c["bs"], cache_dtype=oracle.BF16)
+    kc = torch.from_numpy(kb).view(torch.bfloat16).reshape(host.key_cache.shape)
+    vc = torch.from_numpy(vb).view(torch.bfloat16).reshape(host.value_cache.shape)
     qsl = host.query_start_loc
     worst = 0.0
     for s, j in [(0, 0), (0, 511), (1, 255), (2, 1), (3, 400), (3, 511)]:
         q = int(qsl[s]) + j
-        ref = oracle.prefix_attention(host.query[q:q + 1], host.key[q:q + 1], host.value[q:q + 1], host.key_cache,
-                                      host.value_cache, host.block_tables[s:s + 1],
-                                      torch.tensor([0, 1], dtype=torch.int32),
+        ref = oracle.prefix_attention(host.query[q:q + 1], host.key[q:q + 1], host.value[q:q + 1], kc, vc,
+                                      host.block_tables[s:s + 1], torch.tensor([0, 1], dtype=torch.int32),
                                       torch.tensor([c["ctx"][s] + j], dtype=torch.int32), num_kv_heads=c["KVH"],
                                       block_size=c["bs"], scale=c["d"] ** -0.5, q_dtype=oracle.BF16,
                                       kv_dtype=oracle.BF16)

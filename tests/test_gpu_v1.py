@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import oracle
+import _tol
 import decode_attention_paged_v2_amd as pav2
 from decode_attention_paged_v2_amd import workloads as W
 
@@ -27,7 +28,6 @@ OUT_TOL = {torch.float32: 1e-5, torch.float16: 2e-3, torch.bfloat16: 2e-3}
 FP8_TOL = 1e-2
 GUARD = 4096
 SENTINEL = 4096.0
-MANTISSA_BITS = {torch.float32: 23, torch.float16: 10, torch.bfloat16: 7}
 
 
 def say(msg):
@@ -77,16 +77,6 @@ def max_abs_logit(wl, pairs):
     return {(s, h): float(np.abs(ml[s, h][np.isfinite(ml[s, h])]).max(initial=0.0)) for s, h in pairs}
 
 
-def rne(a, dtype):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).double().numpy()
-
-
-def allowed_error(ref, dtype, tol):
-    a = np.maximum(np.abs(ref), 2.0 ** -126)
-    ulp = 2.0 ** (np.floor(np.log2(a)) - MANTISSA_BITS[dtype])
-    return np.maximum(tol, ulp)
-
-
 def compare(wl, go, ro, pairs=None):
     """Element-by-element check of the V1 output against the dense oracle."""
     if pairs is None:
@@ -100,12 +90,8 @@ def compare(wl, go, ro, pairs=None):
         if L == 0:
             assert np.all(g == 0.0), f"out[{s},{h}] of an empty sequence is not zero"
             continue
-        r = rne(ro[s, h], wl.q_dtype)
         t = tol if mabs is None else tol + 2.0 ** -21 * mabs[(s, h)]
-        err = np.abs(g - r)
-        worst = max(worst, err.max())
-        assert (err <= allowed_error(r, wl.q_dtype, t)).all(), \
-            f"out[{s},{h}] L={L}: max err {err.max():.3g} > {t}"
+        worst = max(worst, _tol.check(g, ro[s, h], wl.q_dtype, t, f"out[{s},{h}] L={L}"))
     return worst
 
 

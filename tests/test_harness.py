@@ -72,3 +72,23 @@ def test_bench_reads_traffic_only_for_current_sources():
                 assert got == round(data["phase1_traffic_bytes"])
             else:
                 assert got is None
+
+
+def test_source_hash_covers_the_launch_plan(tmp_path, monkeypatch):
+    # the planner (schedule, grid, LDS sizing, scale folding) lives in api.hip
+    # and the ABI's constants in pav2.h: editing either must invalidate the
+    # stored counters, as editing a kernel does
+    for mode in ("decode", "cache_write"):
+        names = [os.path.basename(f) for f in H.KERNEL_SOURCES[mode]]
+        assert "api.hip" in names and "pav2.h" in names
+    assert any(n.startswith("phase1_") for n in map(os.path.basename, H.KERNEL_SOURCES["decode"]))
+    copies = []
+    for f in H.KERNEL_SOURCES["decode"]:
+        dst = tmp_path / os.path.basename(f)
+        dst.write_bytes(open(f, "rb").read())
+        copies.append(str(dst))
+    monkeypatch.setitem(H.KERNEL_SOURCES, "decode", copies)
+    before = H.source_hash("decode")
+    api = tmp_path / "api.hip"
+    api.write_bytes(api.read_bytes() + b"\n// planner edit\n")
+    assert H.source_hash("decode") != before
