@@ -56,6 +56,10 @@ def load():
         L.pav2_paged_attention_v2.restype = I
         L.pav2_paged_attention_v1.argtypes = [P, P, P, P, I, F, P, P, I, I, P, I, F, F, I, I, I, I, I, I, P]
         L.pav2_paged_attention_v1.restype = I
+        L.pav2_paged_attention_v2_noalloc.argtypes = [P, P, P, P, I, F, P, P, I, I, P, I, F, F, I, I, I, I, I, I, P]
+        L.pav2_paged_attention_v2_noalloc.restype = I
+        L.pav2_noalloc_scratch_bytes.argtypes = []
+        L.pav2_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.pav2_phase1.argtypes = attn[1:]
         L.pav2_phase1.restype = I
         L.pav2_phase2.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
@@ -187,6 +191,31 @@ def paged_attention_v1(output, query, key_cache, value_cache, num_kv_heads, scal
         S, H, D, int(key_cache.shape[0]), int(block_tables.shape[1]), _dtype_code(query),
         _stream(query, stream))
     _check(rc)
+
+
+def paged_attention_v2_noalloc(output, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+                               seq_lens, block_size, max_seq_len, alibi_slopes=None, kv_cache_dtype="auto",
+                               k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """V2 with the partition workspace in the library's per-device scratch
+    (pav2_paged_attention_v2_noalloc): fills output in place, allocates nothing.
+    Calls that overlap on one GPU share that scratch and race."""
+    L = load()
+    S, H, D, kvdt = _common(query, key_cache, value_cache, num_kv_heads, block_tables, seq_lens,
+                            block_size, kv_cache_dtype, alibi_slopes)
+    if tuple(output.shape) != (S, H, D) or output.dtype != query.dtype:
+        raise ValueError("output must match query in shape and dtype")
+    rc = L.pav2_paged_attention_v2_noalloc(
+        _dev(output, "output"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), int(num_kv_heads), float(scale),
+        _i32(block_tables, "block_tables"), _i32(seq_lens, "seq_lens"), int(block_size),
+        int(max_seq_len), _dev(alibi_slopes, "alibi_slopes"), kvdt, float(k_scale), float(v_scale),
+        S, H, D, int(key_cache.shape[0]), int(block_tables.shape[1]), _dtype_code(query),
+        _stream(query, stream))
+    _check(rc)
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().pav2_noalloc_scratch_bytes())
 
 
 def phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, num_kv_heads, scale,

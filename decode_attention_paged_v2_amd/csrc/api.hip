@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/pav2.h"
 #include "pav2_internal.h"
 #include "cache.h"
@@ -244,6 +246,49 @@ int check_phase1_args(float *exp_sums, float *max_logits, void *tmp_output, cons
     return PAV2_OK;
 }
 
+// ---- the allocation-free V2 entry point's workspace -------------------------
+//
+// pav2_paged_attention_v2_noalloc keeps phase 1's partition workspace
+// (tmp_output, exp_sums, max_logits) in this file-scope device array instead
+// of caller buffers.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never passes `scratch` itself (on the host it
+// is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device on that device's first call.
+constexpr size_t kScratchBytes = (size_t)64 << 20;   // 64 MiB
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Bytes of partition workspace a problem needs in the scratch layout
+// [tmp_output | exp_sums | max_logits], each part 256-byte aligned.
+size_t noalloc_workspace_bytes(const Shape &sh) {
+    const size_t slots = (size_t)sh.num_seqs * sh.num_heads * sh.max_num_partitions;
+    return round256(slots * sh.head_size * elem_bytes(sh.qdt)) + 2 * round256(slots * sizeof(float));
+}
+
+// The calling thread's current device's copy of `scratch`.
+int scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PAV2_ERR_LAUNCH, "hipGetDevice: HIP error %d (%s)", (int)e, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(PAV2_ERR_UNSUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(PAV2_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: HIP error %d (%s)", dev, (int)e,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return PAV2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -337,6 +382,51 @@ int pav2_paged_attention_v1(void *output, const void *query, const void *key_cac
     return run_v1(output, query, key_cache, value_cache, scale, block_tables, seq_lens, alibi_slopes, k_scale,
                   v_scale, sh, static_cast<hipStream_t>(stream));
 }
+
+int pav2_paged_attention_v2_noalloc(void *output, const void *query, const void *key_cache,
+                                    const void *value_cache, int num_kv_heads, float scale,
+                                    const int32_t *block_tables, const int32_t *seq_lens, int block_size,
+                                    int max_seq_len, const float *alibi_slopes, pav2_dtype_t kv_cache_dtype,
+                                    float k_scale, float v_scale, int num_seqs, int num_heads, int head_size,
+                                    int num_blocks, int max_blocks_per_seq, pav2_dtype_t query_dtype,
+                                    pav2_stream_t stream) {
+    g_err[0] = 0;
+    const int maxp = pav2_max_num_partitions(max_seq_len);
+    Shape sh{num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks,
+             max_blocks_per_seq, maxp > 0 ? maxp : 1, max_seq_len, (int)query_dtype, (int)kv_cache_dtype};
+    int rc = check_shape(sh);
+    if (rc) return rc;
+    if (num_seqs == 0) return PAV2_OK;
+    if (!output || !query || !key_cache || !value_cache || !block_tables || !seq_lens)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (!isfinite(scale) || !isfinite(k_scale) || !isfinite(v_scale))
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "scale, k_scale and v_scale must be finite");
+    const size_t need = noalloc_workspace_bytes(sh);
+    if (need > kScratchBytes)
+        return fail(PAV2_ERR_UNSUPPORTED,
+                    "the partition workspace of num_seqs %d x num_heads %d x %d partitions x head_size %d needs "
+                    "%zu bytes, beyond the %zu-byte scratch of pav2_paged_attention_v2_noalloc; call "
+                    "pav2_paged_attention_v2 with caller-allocated buffers",
+                    num_seqs, num_heads, sh.max_num_partitions, head_size, need, kScratchBytes);
+    void *base = nullptr;
+    rc = scratch_address(&base);
+    if (rc) return rc;
+    const size_t slots = (size_t)num_seqs * num_heads * sh.max_num_partitions;
+    uint8_t *b = static_cast<uint8_t *>(base);
+    void *tmp_output = b;
+    float *exp_sums = reinterpret_cast<float *>(b + round256(slots * head_size * elem_bytes(query_dtype)));
+    float *max_logits = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(exp_sums) + round256(slots * sizeof(float)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // phase 1 writes every slot's statistics and every used slot's output row;
+    // phase 2 reads only those, so nothing left from an earlier call is read
+    rc = run_phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, scale, block_tables, seq_lens,
+                    alibi_slopes, k_scale, v_scale, sh, st);
+    if (rc) return rc;
+    return run_phase2(output, exp_sums, max_logits, tmp_output, seq_lens, num_seqs, num_heads, head_size,
+                      sh.max_num_partitions, (int)query_dtype, st);
+}
+
+size_t pav2_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int pav2_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
               int max_num_partitions, pav2_dtype_t query_dtype, pav2_dtype_t kv_cache_dtype,

@@ -55,6 +55,7 @@
 #ifndef PAV2_H
 #define PAV2_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -139,6 +140,43 @@ int pav2_paged_attention_v1(
     int max_blocks_per_seq,
     pav2_dtype_t query_dtype,
     pav2_stream_t stream);
+
+/*
+ * PagedAttention V2 for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same two launches and the same output as
+ * pav2_paged_attention_v2, with phase 1's partition workspace (tmp_output,
+ * exp_sums, max_logits) held in a library-owned static device array instead
+ * of caller buffers.  Arguments as pav2_paged_attention_v1 (the caller passes
+ * the inputs and `output` only); max_num_partitions = ceil(max_seq_len / 512).
+ *
+ * Limit: the workspace, num_seqs * num_heads * max_num_partitions *
+ * (head_size * sizeof(query element) + 8) bytes (each of its three parts
+ * rounded up to 256 bytes), must fit the scratch of
+ * pav2_noalloc_scratch_bytes() = 64 MiB; larger problems return
+ * PAV2_ERR_UNSUPPORTED before any HIP call.  Each GPU holds one copy of the
+ * scratch from its first call until the process ends (the calling thread's
+ * current device, which must be the stream's); this entry point calls no
+ * hipMalloc / hipFree.  Every call on one GPU shares that copy: calls that
+ * overlap on one GPU (other streams, other threads) race and must be ordered
+ * by the caller.  Nothing in it needs clearing between calls (phase 1 writes
+ * every slot phase 2 reads).
+ */
+int pav2_paged_attention_v2_noalloc(
+    void *output,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_kv_heads, float scale,
+    const int32_t *block_tables, const int32_t *seq_lens,
+    int block_size, int max_seq_len,
+    const float *alibi_slopes,
+    pav2_dtype_t kv_cache_dtype, float k_scale, float v_scale,
+    int num_seqs, int num_heads, int head_size, int num_blocks,
+    int max_blocks_per_seq,
+    pav2_dtype_t query_dtype,
+    pav2_stream_t stream);
+
+/* Size in bytes of pav2_paged_attention_v2_noalloc's per-device scratch. */
+size_t pav2_noalloc_scratch_bytes(void);
 
 /*
  * Phase 1 alone (same arguments as pav2_paged_attention_v2 without `output`): writes

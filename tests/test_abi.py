@@ -276,3 +276,40 @@ def test_prefix_attention_validation():
     assert call(context_lens=None) == -1
     assert call(num_seqs=0, output=None, query=None) == 0   # nothing to do
     assert call(max_query_len=0, output=None) == 0
+
+
+def _call_noalloc(**over):
+    """pav2_paged_attention_v2_noalloc with host-only pointers and overridable sizes."""
+    lib = pav2.load()
+    a = dict(output=ctypes.c_void_p(16), query=ctypes.c_void_p(16), key_cache=ctypes.c_void_p(16),
+             value_cache=ctypes.c_void_p(16), num_kv_heads=8, scale=0.0625,
+             block_tables=ctypes.c_void_p(16), seq_lens=ctypes.c_void_p(16), block_size=16,
+             max_seq_len=32768, alibi_slopes=None, kv_cache_dtype=B.F16, k_scale=1.0, v_scale=1.0,
+             num_seqs=256, num_heads=32, head_size=80, num_blocks=600000, max_blocks_per_seq=2048,
+             query_dtype=B.F16, stream=None)
+    a.update(over)
+    return lib.pav2_paged_attention_v2_noalloc(*a.values())
+
+
+def test_noalloc_scratch_limit_is_checked_before_any_hip_call():
+    # 256 seqs x 32 heads x 64 partitions x (80 * 2 + 8) bytes = 88 MB of
+    # partition workspace does not fit the 64 MiB scratch: rejected up front
+    assert pav2.noalloc_scratch_bytes() == 64 << 20
+    assert _call_noalloc() == -2
+    msg = pav2.last_error()
+    assert "scratch" in msg and "pav2_paged_attention_v2 with caller-allocated buffers" in msg
+    # the same shape checks as the other entry points
+    assert _call_noalloc(num_heads=33) == -1 and "multiple of num_kv_heads" in pav2.last_error()
+    assert _call_noalloc(output=None, num_seqs=4) == -1 and "NULL" in pav2.last_error()
+    assert _call_noalloc(num_seqs=0, output=None) == 0
+
+
+def test_noalloc_workspace_bound_is_exact():
+    # the largest batch whose workspace fits: tmp rows + two float32 statistics per slot,
+    # each part rounded up to 256 bytes
+    def need(S, H, P, D, b):
+        r = lambda n: (n + 255) // 256 * 256
+        return r(S * H * P * D * b) + 2 * r(S * H * P * 4)
+    S_fit = max(S for S in range(1, 400) if need(S, 32, 64, 80, 2) <= 64 << 20)
+    assert need(S_fit + 1, 32, 64, 80, 2) > 64 << 20
+    assert _call_noalloc(num_seqs=S_fit + 1) == -2
