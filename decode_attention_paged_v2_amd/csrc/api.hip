@@ -88,9 +88,9 @@ int check_shape(const Shape &s) {
     if (s.kvdt != s.qdt && s.kvdt != PAV2_FP8_E4M3)
         return fail(PAV2_ERR_UNSUPPORTED, "query dtype %s with kv dtype %s is not supported",
                     dt_name(s.qdt), dt_name(s.kvdt));
-    if (ilog2_exact(s.block_size) < 3 || PAV2_PARTITION_SIZE % s.block_size)
+    if (s.block_size < 1 || s.block_size > PAV2_PARTITION_SIZE || PAV2_PARTITION_SIZE % s.block_size)
         return fail(PAV2_ERR_INVALID_ARGUMENT,
-                    "block_size %d must be a power of two in [8, 512] dividing the 512-token partition",
+                    "block_size %d must divide the 512-token partition (a power of two in [1, 512])",
                     s.block_size);
     if (s.num_blocks <= 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
     if (s.max_seq_len < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 0");
@@ -538,8 +538,8 @@ int pav2_reshape_and_cache(const void *key, const void *value, void *key_cache, 
         return fail(PAV2_ERR_UNSUPPORTED, "head_size %d is not a multiple of x = %d for %s", head_size, x,
                     dt_name(kv_cache_dtype));
     const int bs_log2 = ilog2_exact(block_size);
-    if (bs_log2 < 3 || bs_log2 > 9)
-        return fail(PAV2_ERR_UNSUPPORTED, "block_size %d must be a power of two in [8, 512]", block_size);
+    if (bs_log2 < 0 || bs_log2 > 9)
+        return fail(PAV2_ERR_INVALID_ARGUMENT, "block_size %d must be a power of two in [1, 512]", block_size);
     if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale))
         return fail(PAV2_ERR_INVALID_ARGUMENT, "k_scale (%g) and v_scale (%g) must be finite and > 0",
                     (double)k_scale, (double)v_scale);

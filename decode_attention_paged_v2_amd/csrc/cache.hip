@@ -28,9 +28,9 @@
 // * stores: keys token-fastest (tokens with consecutive slots give
 //   block_size * 16 contiguous bytes per chunk); values as 8 tokens of one
 //   head-dim row per lane (gathered from the 8 token rows in LDS), one
-//   vector store when their slots are 8 consecutive, 8-aligned positions
-//   (always within one block, as block sizes are powers of two >= 8), else
-//   element by element.
+//   vector store when their slots are 8 consecutive, 8-aligned positions in
+//   a block of at least 8 tokens (then always within one block, as block
+//   sizes are powers of two), else element by element.
 #include "cache.h"
 
 namespace pav2 {
@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(kCacheThreads) cache_write_kernel(const CacheP
             sl[k] = s_slot[8 * h + k];
             run = run && sl[k] >= 0 && sl[k] == sl[0] + k;
         }
-        run = run && (sl[0] & 7) == 0;
+        run = run && (sl[0] & 7) == 0 && bs_log2 >= 3;   // 8 aligned slots share one block of >= 8
         uint8_t *vbase = P.value_cache + head_off;
         for (int i = tid / NG; i < D; i += kCacheThreads / NG) {
             // element i of tokens 8h .. 8h+7, packed in words

@@ -154,7 +154,8 @@ __device__ __forceinline__ T load_stream(const uint8_t *p) {
 // SCHED: 0 dense grid of partition slots, 1 compact list of used partitions,
 // 2 single pass (one workgroup per (sequence, kv head, head group) walks all
 // of the sequence's partitions and writes the final output).
-// BS: the block size when fixed at compile time (16 or 32), 0 for any.
+// BS: the block size when fixed at compile time (16 or 32), 0 for any of
+// 8 .. 512, -1 for 1, 2 or 4 (a lane's 8-token V slice then spans blocks).
 template <int QDT, int KVDT, int D, int WAVES, int SCHED, int BS>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(kPhase1Occupancy)))
 phase1_kernel(const Phase1Params P) {
@@ -283,7 +284,7 @@ phase1_kernel(const Phase1Params P) {
     }
 
     // Single pass: the merging threads carry, per output vector they own, the
-    // running maximum (log2 units, absolute position frame), the rounded-weight
+    // running maximum (log2 units; with ALiBi relative to the last token), the rounded-weight
     // sum and the unnormalised output of the partitions merged so far.
     constexpr int VEC = QDT == F32 ? 4 : 8;
     constexpr int PER_HEAD = D / VEC;
@@ -463,6 +464,40 @@ phase1_kernel(const Phase1Params P) {
     auto load_v = [&](Words<VW> (&dst)[DPG], int u, int part) {
         const int t = clamp_unit(unit_of(u));
         const int o = t * UNIT + 8 * grp;                    // first of the lane's 8 tokens
+        if constexpr (BS < 0) {
+            // blocks of 1, 2 or 4 tokens: the lane's 8 tokens span 8 / block_size
+            // blocks, so each token's element comes from its own block's row
+            const uint8_t *tb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tok = o + e;
+                tb[e] = vc + (int64_t)s_bt[tok >> bs_log2] * blk_stride + ((tok & bs_mask) + (col << bs_log2)) * KVB;
+            }
+#pragma unroll
+            for (int i = 0; i < DPG; ++i) {
+                const int dt = part * DPG + i;
+                if (dt >= NDT) break;
+                const bool ok = (D % 16 == 0) || (16 * dt + col < D);
+                const int64_t roff = ((int64_t)(16 * dt) << bs_log2) * KVB;
+                uint32_t el[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint32_t v = 0u;
+                    if (ok) {
+                        if constexpr (KVB == 4) v = *reinterpret_cast<const uint32_t *>(tb[e] + roff);
+                        else if constexpr (KVB == 2) v = *reinterpret_cast<const uint16_t *>(tb[e] + roff);
+                        else v = *(tb[e] + roff);
+                    }
+                    el[e] = v;
+                }
+#pragma unroll
+                for (int w = 0; w < VW; ++w) {
+                    if constexpr (KVB == 4) dst[i].w[w] = el[w];
+                    else if constexpr (KVB == 2) dst[i].w[w] = el[2 * w] | (el[2 * w + 1] << 16);
+                    else dst[i].w[w] = el[4 * w] | (el[4 * w + 1] << 8) | (el[4 * w + 2] << 16) | (el[4 * w + 3] << 24);
+                }
+            }
+        } else {
         const uint8_t *base;
         if constexpr (BS >= 32) {
             // the unit's 32 tokens share one block
@@ -495,6 +530,7 @@ phase1_kernel(const Phase1Params P) {
                     dst[i].w[4 * h + 3] = v[3];
                 }
             }
+        }
         }
     };
 
@@ -776,7 +812,12 @@ phase1_kernel(const Phase1Params P) {
                 const int d0 = (idx - hh * PER_HEAD) * VEC;
                 float M, l, lr, a[VEC];
                 combine(hh, d0, M, l, lr, a);
-                if (!PREFIX && P.alibi != nullptr) M += P.alibi[h0 + hh] * kLog2e * (float)last;
+                // ALiBi: partition maxima are relative to the partition's last
+                // token; the running merge takes them relative to the
+                // sequence's last token (nothing is stored, so any per-head
+                // frame serves), where the partitions that carry weight have
+                // small maxima and float32 resolves their differences finely
+                if (!PREFIX && P.alibi != nullptr) M += P.alibi[h0 + hh] * kLog2e * (float)(last - (L - 1));
                 const float Mn = fmaxf(run_m[k], M);
                 const float fo = exp2_fast(run_m[k] - Mn);   // 0 for the first partition
                 const float fn = exp2_fast(M - Mn);
@@ -925,10 +966,12 @@ hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
 
 // Block sizes 16 and 32 (16-bit queries) get kernels with the block size
 // fixed at compile time (load offsets become immediates; the block of a
-// 16-token K tile, and at 32 of a whole unit, is wave-uniform); every other
-// case runs the generic kernel.
+// 16-token K tile, and at 32 of a whole unit, is wave-uniform); blocks of 1,
+// 2 or 4 tokens a kernel whose V gather takes each token from its own block
+// (BS = -1); every other case runs the generic kernel.
 template <int QDT, int KVDT, int D, int SCHED>
 hipError_t launch_bs(const Phase1Params &p, int lds, hipStream_t stream) {
+    if (p.bs_log2 < 3) return launch_sched<QDT, KVDT, D, SCHED, -1>(p, lds, stream);   // blocks of 1, 2, 4
     if constexpr (QDT != F32) {
         if (p.bs_log2 == 4) return launch_sched<QDT, KVDT, D, SCHED, 16>(p, lds, stream);
         if (p.bs_log2 == 5) return launch_sched<QDT, KVDT, D, SCHED, 32>(p, lds, stream);

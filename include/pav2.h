@@ -92,8 +92,9 @@ typedef void *pav2_stream_t; /* hipStream_t */
  * metadata follow, then the query dtype and the stream.
  *
  * Supported: head_size in {64, 80, 96, 112, 120, 128, 192, 256} (the pages'
- * supported head sizes) with head_size % x == 0; block_size a power of two in
- * [8, 512] (512 % block_size == 0); num_heads % num_kv_heads == 0;
+ * supported head sizes) with head_size % x == 0; block_size any divisor of
+ * the 512-token partition (1, 2, 4, ..., 512: page "paged_attn.py",
+ * forward_decode, asserts 512 % block_size == 0); num_heads % num_kv_heads == 0;
  * (query_dtype, kv_cache_dtype) in {(F32, F32), (F16, F16), (BF16, BF16),
  * (F32, FP8_E4M3), (F16, FP8_E4M3), (BF16, FP8_E4M3)};
  * max_num_partitions >= ceil(max_seq_len / 512) and <= 16384;

@@ -60,8 +60,9 @@ INVALID = [
     (dict(head_size=120, kv_cache_dtype=B.FP8_E4M3), -2, "multiple of x = 16"),
     (dict(block_size=24), -1, "block_size 24"),
     (dict(block_size=1024), -1, "block_size 1024"),
-    (dict(block_size=2), -1, "block_size 2"),
-    (dict(block_size=4), -1, "block_size 4"),
+    (dict(block_size=3), -1, "block_size 3"),
+    (dict(block_size=0), -1, "block_size 0"),
+    (dict(block_size=48), -1, "block_size 48"),
     (dict(max_num_partitions=195), -1, "ceil(max_seq_len / 512) = 196"),
     (dict(max_blocks_per_seq=6249), -1, "max_blocks_per_seq"),
     (dict(query_dtype=B.F16), -2, "query dtype f16 with kv dtype bf16"),
@@ -230,8 +231,10 @@ def test_reshape_and_cache_validation():
     assert call(kv_cache_dtype=B.F16) == -2                       # neither the input dtype nor fp8
     assert call(head_size=100) == -2
     assert call(head_size=120, kv_cache_dtype=B.FP8_E4M3) == -2   # 120 % 16 != 0
-    assert call(block_size=24) == -2
-    assert call(block_size=4) == -2
+    assert call(block_size=24) == -1                              # not a power of two
+    assert call(block_size=1024) == -1
+    assert call(block_size=0) == -1
+    assert call(block_size=4, num_tokens=0) == 0                  # blocks of 1, 2, 4 are accepted
     assert call(k_scale=0.0) == -1
     assert call(v_scale=float("inf")) == -1
     assert call(k_scale=float("nan")) == -1

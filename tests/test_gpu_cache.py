@@ -101,7 +101,7 @@ def test_write_matches_oracle(in_dt, cache_dt, d, pattern):
     assert_same_bytes(gv, rv)
 
 
-@pytest.mark.parametrize("bs", [8, 32, 64, 512])
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 64, 512])
 @pytest.mark.parametrize("in_dt,cache_dt", [("bf16", "bf16"), ("f16", "fp8_e4m3"), ("f32", "f32")])
 def test_write_block_sizes(bs, in_dt, cache_dt):
     print(f"case bs={bs} {in_dt}->{cache_dt}", flush=True)

@@ -174,7 +174,9 @@ def test_parity_full_size_sampled(name):
 
 @pytest.mark.parametrize("kv,q,BS", [("f16", "f16", 16), ("bf16", "bf16", 8), ("f32", "f32", 8),
                                      ("fp8_e4m3", "bf16", 32), ("fp8_e4m3", "f16", 64),
-                                     ("bf16", "bf16", 128), ("fp8_e4m3", "f32", 16)])
+                                     ("bf16", "bf16", 128), ("fp8_e4m3", "f32", 16),
+                                     ("f16", "f16", 1), ("fp8_e4m3", "bf16", 2), ("f32", "f32", 4),
+                                     ("bf16", "bf16", 4)])
 def test_block_table_one_hot_probe(kv, q, BS):
     """Sequence s has K = 0 except its token tau = s, where K[tau, 0] = c with
     scale * c = 200 (q = e_0): the softmax weight of every other token underflows
@@ -276,10 +278,26 @@ def test_edge_dtypes_head_sizes(q, kv, D):
     compare(wl, g, run_oracle(wl))
 
 
-@pytest.mark.parametrize("BS", [8, 32, 64, 128, 256, 512])
+@pytest.mark.parametrize("BS", [1, 2, 4, 8, 32, 64, 128, 256, 512])
 def test_edge_block_sizes(BS):
-    spec = W.Spec(f"bs{BS}", 8, 2, 128, BS, "f16", "f16", lambda g: [1, BS - 1, BS, BS + 1, 1300, 0],
+    spec = W.Spec(f"bs{BS}", 8, 2, 128, BS, "f16", "f16", lambda g: [1, max(BS - 1, 0), BS, BS + 1, 1300, 0, 7],
                   pool=lambda n: n + 3, alibi=True, seed=BS)
+    wl = W.generate(spec, poison=True)
+    g = run_gpu(wl.to(DEV))
+    compare(wl, g, run_oracle(wl))
+
+
+@pytest.mark.parametrize("q,kv", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
+                                  ("f32", "fp8_e4m3"), ("f16", "fp8_e4m3"), ("bf16", "fp8_e4m3")])
+@pytest.mark.parametrize("BS", [1, 2, 4])
+def test_small_blocks_every_dtype_pair(q, kv, BS):
+    """Blocks of 1, 2 or 4 tokens (the pages only ask that the block size divide
+    the 512-token partition): a lane's 8-token V slice then spans several
+    blocks.  Ragged lengths across partitions, ALiBi, a non-power-of-two head size."""
+    D = 112
+    ks, vs = (0.05, 0.04) if kv == "fp8_e4m3" else (1.0, 1.0)
+    spec = W.Spec(f"small_{q}_{kv}_{BS}", 8, 2, D, BS, q, kv, lambda g: [0, 1, 3, 9, 511, 513, 1100],
+                  pool=lambda n: n + 9, alibi=True, k_scale=ks, v_scale=vs, seed=100 + BS)
     wl = W.generate(spec, poison=True)
     g = run_gpu(wl.to(DEV))
     compare(wl, g, run_oracle(wl))

@@ -65,7 +65,7 @@ def test_prefix_gqa_row_blocks(H, KVH):
     assert_close(out, ref, "bf16")
 
 
-@pytest.mark.parametrize("BS", [8, 32, 64, 512])
+@pytest.mark.parametrize("BS", [1, 2, 4, 8, 32, 64, 512])
 def test_prefix_block_sizes(BS):
     print(f"case prefix block {BS}", flush=True)
     out, ref = run_case([17, 600], [30, 12], 8, 2, 64, BS, "bf16", seed=BS)

@@ -149,7 +149,7 @@ def test_v1_edge_dtypes_head_sizes(q, kv, D):
     compare(wl, run_v1(wl.to(DEV)), run_dense(wl))
 
 
-@pytest.mark.parametrize("BS", [8, 16, 32, 64, 256, 512])
+@pytest.mark.parametrize("BS", [1, 2, 4, 8, 16, 32, 64, 256, 512])
 def test_v1_edge_block_sizes(BS):
     spec = W.Spec(f"v1_bs{BS}", 8, 2, 128, BS, "bf16", "bf16", lambda g: [1, BS - 1, BS, BS + 1, 1300, 0],
                   pool=lambda n: n + 3, alibi=True, seed=BS)
@@ -230,3 +230,16 @@ def test_forward_decode_dispatch(lens, expect_v1):
                               d.num_kv_heads, d.scale, d.block_size, d.max_seq_len,
                               alibi_slopes=d.alibi_slopes).cpu()
     compare(wl, out, run_dense(wl))
+
+
+def test_v1_alibi_long_context_frame():
+    """ALiBi at 200 partitions plus one token: slopes up to 0.5 put the absolute
+    partition maxima near 7e4 (log2 units), where float32 steps are 2^-7, yet
+    the output depends on the last two partitions' relative weights.  The
+    single pass merges them relative to the sequence's last token."""
+    L = 200 * 512 + 1
+    spec = W.Spec("v1_alibi_long", 8, 2, 64, 16, "f16", "f16", lambda g: [L, 513], pool=lambda n: n + 3,
+                  alibi=True, seed=31)
+    wl = W.generate(spec, poison=True)
+    worst = compare(wl, run_v1(wl.to(DEV)), run_dense(wl))
+    say(f"  worst {worst:.3g}")
