@@ -55,7 +55,7 @@ def _load():
             F = ctypes.c_float
             lib.oracle_decode.argtypes = [I, P, ctypes.c_int64, P]
             lib.oracle_decode.restype = I
-            lib.oracle_paged_attention_v2.argtypes = [
+            lib.oracle_paged_attention_v2_blocksparse.argtypes = [
                 P, P, P, P,            # out, max_logits, exp_sums, tmp_out
                 P, I,                  # query, q_dtype
                 P, P, I,               # key_cache, value_cache, kv_dtype
@@ -63,9 +63,10 @@ def _load():
                 P, P,                  # seq_lens, alibi_slopes
                 I, I, I, I, I,         # num_seqs, num_heads, num_kv_heads, head_size, block_size
                 I, F, F, F,            # max_num_partitions, scale, k_scale, v_scale
+                I, I, I, I, I,         # tp_rank, local_blocks, vert_stride, sparse block size, sliding step
                 P, I]                  # pair_mask, num_threads
-            lib.oracle_paged_attention_v2.restype = I
-            lib.oracle_dense_attention.argtypes = [
+            lib.oracle_paged_attention_v2_blocksparse.restype = I
+            lib.oracle_dense_attention_blocksparse.argtypes = [
                 P,
                 P, I,
                 P, P, I,
@@ -73,8 +74,9 @@ def _load():
                 P, P,
                 I, I, I, I, I,
                 F, F, F,
+                I, I, I, I, I,
                 P, I]
-            lib.oracle_dense_attention.restype = I
+            lib.oracle_dense_attention_blocksparse.restype = I
             lib.oracle_encode.argtypes = [I, P, ctypes.c_int64, P]
             lib.oracle_encode.restype = I
             lib.oracle_reshape_and_cache.argtypes = [
@@ -145,16 +147,25 @@ def _common(query, key_cache, value_cache, block_tables, seq_lens, alibi_slopes)
     return q, kc, vc, bt, sl, al
 
 
+def _sparse_args(tp_rank, local_blocks, vert_stride, bs_block_size, head_sliding_step):
+    return (int(tp_rank), int(local_blocks), int(vert_stride or 0), int(bs_block_size), int(head_sliding_step))
+
+
 def paged_attention_v2(query, key_cache, value_cache, block_tables, seq_lens, *,
                        num_kv_heads, scale, block_size, max_num_partitions,
                        q_dtype, kv_dtype, alibi_slopes=None, k_scale=1.0,
-                       v_scale=1.0, pairs=None, threads=None):
+                       v_scale=1.0, pairs=None, threads=None, tp_rank=0,
+                       blocksparse_local_blocks=0, blocksparse_vert_stride=0,
+                       blocksparse_block_size=64, blocksparse_head_sliding_step=0):
     """Partitioned (V2) decode in float64.
 
     query [S, H, D]; key_cache [NB, KVH, D/x, BS, x]; value_cache [NB, KVH, D, BS]
     (torch tensors or numpy arrays of raw element bytes); block_tables
     [S, max_blocks_per_seq] int32; seq_lens [S] int32.  ``pairs`` optionally
-    lists (s, h) pairs to compute (other rows are returned as NaN).
+    lists (s, h) pairs to compute (other rows are returned as NaN).  The
+    block-sparse arguments (the V2 op's, with its defaults) select the
+    block-sparse pattern when blocksparse_vert_stride > 1 (see
+    pav2_oracle.c for the reading taken).
 
     Returns a dict of float64 arrays: out [S,H,D], max_logits [S,H,P],
     exp_sums [S,H,P], tmp_output [S,H,P,D].
@@ -172,12 +183,14 @@ def paged_attention_v2(query, key_cache, value_cache, block_tables, seq_lens, *,
         mask = np.zeros(S * H, dtype=np.uint8)
         for s, h in pairs:
             mask[int(s) * H + int(h)] = 1
-    rc = lib.oracle_paged_attention_v2(
+    rc = lib.oracle_paged_attention_v2_blocksparse(
         _ptr(out), _ptr(ml), _ptr(es), _ptr(to),
         _ptr(q), q_dtype, _ptr(kc), _ptr(vc), kv_dtype,
         _ptr(bt), bt.shape[1], _ptr(sl), _ptr(al),
         S, H, int(num_kv_heads), D, int(block_size),
         maxP, float(scale), float(k_scale), float(v_scale),
+        *_sparse_args(tp_rank, blocksparse_local_blocks, blocksparse_vert_stride, blocksparse_block_size,
+                      blocksparse_head_sliding_step),
         _ptr(mask), _threads(threads))
     if rc != 0:
         raise ValueError(f"oracle_paged_attention_v2 rejected its arguments (rc={rc})")
@@ -187,8 +200,10 @@ def paged_attention_v2(query, key_cache, value_cache, block_tables, seq_lens, *,
 def dense_attention(query, key_cache, value_cache, block_tables, seq_lens, *,
                     num_kv_heads, scale, block_size, q_dtype, kv_dtype,
                     alibi_slopes=None, k_scale=1.0, v_scale=1.0, pairs=None,
-                    threads=None):
-    """Unpartitioned decode (one softmax over every token) in float64: out [S,H,D]."""
+                    threads=None, tp_rank=0, blocksparse_local_blocks=0,
+                    blocksparse_vert_stride=0, blocksparse_block_size=64,
+                    blocksparse_head_sliding_step=0):
+    """Unpartitioned decode (one softmax over every attended token) in float64: out [S,H,D]."""
     lib = _load()
     q, kc, vc, bt, sl, al = _common(query, key_cache, value_cache, block_tables, seq_lens, alibi_slopes)
     S, H, D = (int(v) for v in query.shape)
@@ -198,11 +213,13 @@ def dense_attention(query, key_cache, value_cache, block_tables, seq_lens, *,
         mask = np.zeros(S * H, dtype=np.uint8)
         for s, h in pairs:
             mask[int(s) * H + int(h)] = 1
-    rc = lib.oracle_dense_attention(
+    rc = lib.oracle_dense_attention_blocksparse(
         _ptr(out), _ptr(q), q_dtype, _ptr(kc), _ptr(vc), kv_dtype,
         _ptr(bt), bt.shape[1], _ptr(sl), _ptr(al),
         S, H, int(num_kv_heads), D, int(block_size),
         float(scale), float(k_scale), float(v_scale),
+        *_sparse_args(tp_rank, blocksparse_local_blocks, blocksparse_vert_stride, blocksparse_block_size,
+                      blocksparse_head_sliding_step),
         _ptr(mask), _threads(threads))
     if rc != 0:
         raise ValueError(f"oracle_dense_attention rejected its arguments (rc={rc})")

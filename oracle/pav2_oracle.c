@@ -36,6 +36,28 @@
  * "paged_attn.py", _forward_decode_pytorch, reaches the same value), for
  * invariant tests.
  *
+ * Block-sparse V2 (the _blocksparse entry points).  The V2 op takes tp_rank
+ * and four blocksparse_* arguments (page "paged_attention_v2_pytorch.py",
+ * the function's signature; page "paged_attn.py", forward_decode, which takes
+ * the block-sparse branch when blocksparse_vert_stride > 1 and requires
+ * blocksparse_block_size to be a multiple of the cache block size).  The
+ * pages give no body; the reading taken from the names:
+ *
+ *   B = blocksparse_block_size tokens per sparse block; key token t lies in
+ *   sparse block k = t / B, the decode query (position L - 1) in q = (L-1)/B;
+ *   h' = tp_rank * num_heads + h is the head's index in the whole model (a
+ *   tensor-parallel rank holds num_heads consecutive heads);
+ *   query head h attends token t < L iff
+ *     k > q - blocksparse_local_blocks                         (local window)
+ *     or (k - h' * blocksparse_head_sliding_step) mod vert_stride == 0
+ *                                               (vertical stripes, slid per head),
+ *   with the modulo taken into [0, vert_stride).  With vert_stride <= 1 the
+ *   call is dense.  Scores of tokens a head does not attend are excluded from
+ *   its softmax (as the page's -inf padding excludes padded positions);
+ *   a partition with no attended token gets max_logits = -inf, exp_sums = 0,
+ *   tmp_output = 0 and weight 0 in phase 2; a head with no attended token at
+ *   all gets a zero output row, as an empty sequence does.
+ *
  * Element decoding is exact widening to double, written from the formats'
  * definitions: IEEE-754 binary32 and binary16, bfloat16 (the upper half of a
  * binary32), and OCP 8-bit E4M3 ("e4m3fn": bias 7, no infinities, S.1111.111
@@ -156,6 +178,8 @@ typedef struct {
     double *exp_sums;           /* [S, H, maxP] */
     double *tmp_out;            /* [S, H, maxP, D] */
     const uint8_t *pair_mask;   /* [S*H] or NULL: which (s, h) to compute */
+    /* block-sparse pattern (vert_stride <= 1: dense) */
+    int tp_rank, bs_local_blocks, bs_vert_stride, bs_block_size, bs_head_sliding_step;
     int dense;                  /* 1: unpartitioned softmax, 0: V2 partitioned */
     int next_pair;              /* work counter shared by the threads */
 } problem_t;
@@ -175,6 +199,19 @@ static double value_at(const problem_t *P, int s, int g, int t, int i) {
     int64_t blk = P->block_tables[(int64_t)s * P->max_blocks_per_seq + t / bs];
     int64_t idx = (((blk * P->num_kv_heads + g) * P->head_size + i) * bs) + t % bs;
     return dec(P->kv_dtype, P->value_cache, idx) * (double)P->v_scale;
+}
+
+/* Whether query head h of a sequence of length L attends key token t (the
+ * block-sparse reading above; every token when the call is dense). */
+static int attended(const problem_t *P, int h, int L, int t) {
+    if (P->bs_vert_stride <= 1) return 1;
+    int64_t B = P->bs_block_size;
+    int64_t k = t / B, q = (L - 1) / B;
+    if (k > q - P->bs_local_blocks) return 1;
+    int64_t hg = (int64_t)P->tp_rank * P->num_heads + h;
+    int64_t r = (k - hg * P->bs_head_sliding_step) % P->bs_vert_stride;
+    if (r < 0) r += P->bs_vert_stride;
+    return r == 0;
 }
 
 /* Scores z_t for t in [0, L) of query head h (steps 3 and 4). */
@@ -222,15 +259,22 @@ static void solve_pair(const problem_t *P, int s, int h, double *z, double *e) {
             int t0 = p * OR_PARTITION;
             int t1 = t0 + OR_PARTITION < L ? t0 + OR_PARTITION : L;
             double m = -INFINITY;
-            for (int t = t0; t < t1; ++t) m = z[t] > m ? z[t] : m;
+            int any = 0;
+            for (int t = t0; t < t1; ++t)
+                if (attended(P, h, L, t)) {
+                    m = z[t] > m ? z[t] : m;
+                    any = 1;
+                }
+            if (!any) continue;                         /* stays -inf / 0 / 0 */
             double l = 0.0;
             for (int t = t0; t < t1; ++t) {
-                e[t] = exp(z[t] - m);
+                e[t] = attended(P, h, L, t) ? exp(z[t] - m) : 0.0;
                 l += e[t];
             }
             for (int i = 0; i < D; ++i) {
                 double acc = 0.0;
-                for (int t = t0; t < t1; ++t) acc += e[t] * value_at(P, s, g, t, i);
+                for (int t = t0; t < t1; ++t)
+                    if (e[t] != 0.0) acc += e[t] * value_at(P, s, g, t, i);
                 to[(int64_t)p * D + i] = acc / l;
             }
             ml[p] = m;
@@ -238,6 +282,10 @@ static void solve_pair(const problem_t *P, int s, int h, double *z, double *e) {
         }
         double M = -INFINITY;                           /* step 6 */
         for (int p = 0; p < nparts; ++p) M = ml[p] > M ? ml[p] : M;
+        if (M == -INFINITY) {                           /* no attended token at all */
+            for (int i = 0; i < D; ++i) out[i] = 0.0;
+            return;
+        }
         double W = 0.0;
         for (int p = 0; p < nparts; ++p) W += exp(ml[p] - M) * es[p];
         for (int i = 0; i < D; ++i) {
@@ -253,15 +301,21 @@ static void solve_pair(const problem_t *P, int s, int h, double *z, double *e) {
         }
         scores(P, s, h, L, z);
         double M = -INFINITY;
-        for (int t = 0; t < L; ++t) M = z[t] > M ? z[t] : M;
+        for (int t = 0; t < L; ++t)
+            if (attended(P, h, L, t)) M = z[t] > M ? z[t] : M;
+        if (M == -INFINITY) {
+            for (int i = 0; i < D; ++i) out[i] = 0.0;
+            return;
+        }
         double W = 0.0;
         for (int t = 0; t < L; ++t) {
-            e[t] = exp(z[t] - M);
+            e[t] = attended(P, h, L, t) ? exp(z[t] - M) : 0.0;
             W += e[t];
         }
         for (int i = 0; i < D; ++i) {
             double acc = 0.0;
-            for (int t = 0; t < L; ++t) acc += e[t] * value_at(P, s, g, t, i);
+            for (int t = 0; t < L; ++t)
+                if (e[t] != 0.0) acc += e[t] * value_at(P, s, g, t, i);
             out[i] = acc / W;
         }
     }
@@ -302,10 +356,16 @@ static int run(problem_t *P, int num_threads) {
     return 0;
 }
 
+static int check_blocksparse(int tp_rank, int local_blocks, int vert_stride, int bs_block_size, int block_size) {
+    if (vert_stride <= 1) return 0;
+    if (tp_rank < 0 || local_blocks < 0 || bs_block_size <= 0 || bs_block_size % block_size != 0) return -1;
+    return 0;
+}
+
 /* Partitioned (V2) result: out, max_logits, exp_sums, tmp_out, all float64.
  * pair_mask (optional, [S*H]) restricts the work to selected (s, h) pairs;
  * unselected rows of the outputs are left untouched. */
-int oracle_paged_attention_v2(
+int oracle_paged_attention_v2_blocksparse(
     double *out, double *max_logits, double *exp_sums, double *tmp_out,
     const void *query, int q_dtype,
     const void *key_cache, const void *value_cache, int kv_dtype,
@@ -313,7 +373,32 @@ int oracle_paged_attention_v2(
     const int32_t *seq_lens, const float *alibi_slopes,
     int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
     int max_num_partitions, float scale, float k_scale, float v_scale,
+    int tp_rank, int local_blocks, int vert_stride, int bs_block_size, int head_sliding_step,
+    const uint8_t *pair_mask, int num_threads);
+
+int oracle_dense_attention_blocksparse(
+    double *out,
+    const void *query, int q_dtype,
+    const void *key_cache, const void *value_cache, int kv_dtype,
+    const int32_t *block_tables, int max_blocks_per_seq,
+    const int32_t *seq_lens, const float *alibi_slopes,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+    float scale, float k_scale, float v_scale,
+    int tp_rank, int local_blocks, int vert_stride, int bs_block_size, int head_sliding_step,
+    const uint8_t *pair_mask, int num_threads);
+
+int oracle_paged_attention_v2_blocksparse(
+    double *out, double *max_logits, double *exp_sums, double *tmp_out,
+    const void *query, int q_dtype,
+    const void *key_cache, const void *value_cache, int kv_dtype,
+    const int32_t *block_tables, int max_blocks_per_seq,
+    const int32_t *seq_lens, const float *alibi_slopes,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+    int max_num_partitions, float scale, float k_scale, float v_scale,
+    int tp_rank, int local_blocks, int vert_stride, int bs_block_size, int head_sliding_step,
     const uint8_t *pair_mask, int num_threads) {
+    if (block_size <= 0 || check_blocksparse(tp_rank, local_blocks, vert_stride, bs_block_size, block_size))
+        return -1;
     problem_t P;
     memset(&P, 0, sizeof(P));
     P.query = query; P.key_cache = key_cache; P.value_cache = value_cache;
@@ -325,13 +410,31 @@ int oracle_paged_attention_v2(
     P.scale = scale; P.k_scale = k_scale; P.v_scale = v_scale;
     P.out = out; P.max_logits = max_logits; P.exp_sums = exp_sums; P.tmp_out = tmp_out;
     P.pair_mask = pair_mask; P.dense = 0;
+    P.tp_rank = tp_rank; P.bs_local_blocks = local_blocks; P.bs_vert_stride = vert_stride;
+    P.bs_block_size = bs_block_size; P.bs_head_sliding_step = head_sliding_step;
     for (int s = 0; s < num_seqs; ++s)
         if ((seq_lens[s] + OR_PARTITION - 1) / OR_PARTITION > max_num_partitions) return -2;
     return run(&P, num_threads);
 }
 
-/* Unpartitioned result: one softmax over all tokens of each (s, h). */
-int oracle_dense_attention(
+int oracle_paged_attention_v2(
+    double *out, double *max_logits, double *exp_sums, double *tmp_out,
+    const void *query, int q_dtype,
+    const void *key_cache, const void *value_cache, int kv_dtype,
+    const int32_t *block_tables, int max_blocks_per_seq,
+    const int32_t *seq_lens, const float *alibi_slopes,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+    int max_num_partitions, float scale, float k_scale, float v_scale,
+    const uint8_t *pair_mask, int num_threads) {
+    return oracle_paged_attention_v2_blocksparse(
+        out, max_logits, exp_sums, tmp_out, query, q_dtype, key_cache, value_cache, kv_dtype,
+        block_tables, max_blocks_per_seq, seq_lens, alibi_slopes, num_seqs, num_heads, num_kv_heads,
+        head_size, block_size, max_num_partitions, scale, k_scale, v_scale, 0, 0, 0, 1, 0,
+        pair_mask, num_threads);
+}
+
+/* Unpartitioned result: one softmax over all (attended) tokens of each (s, h). */
+int oracle_dense_attention_blocksparse(
     double *out,
     const void *query, int q_dtype,
     const void *key_cache, const void *value_cache, int kv_dtype,
@@ -339,7 +442,10 @@ int oracle_dense_attention(
     const int32_t *seq_lens, const float *alibi_slopes,
     int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
     float scale, float k_scale, float v_scale,
+    int tp_rank, int local_blocks, int vert_stride, int bs_block_size, int head_sliding_step,
     const uint8_t *pair_mask, int num_threads) {
+    if (block_size <= 0 || check_blocksparse(tp_rank, local_blocks, vert_stride, bs_block_size, block_size))
+        return -1;
     problem_t P;
     memset(&P, 0, sizeof(P));
     P.query = query; P.key_cache = key_cache; P.value_cache = value_cache;
@@ -350,7 +456,24 @@ int oracle_dense_attention(
     P.max_blocks_per_seq = max_blocks_per_seq;
     P.scale = scale; P.k_scale = k_scale; P.v_scale = v_scale;
     P.out = out; P.pair_mask = pair_mask; P.dense = 1;
+    P.tp_rank = tp_rank; P.bs_local_blocks = local_blocks; P.bs_vert_stride = vert_stride;
+    P.bs_block_size = bs_block_size; P.bs_head_sliding_step = head_sliding_step;
     return run(&P, num_threads);
+}
+
+int oracle_dense_attention(
+    double *out,
+    const void *query, int q_dtype,
+    const void *key_cache, const void *value_cache, int kv_dtype,
+    const int32_t *block_tables, int max_blocks_per_seq,
+    const int32_t *seq_lens, const float *alibi_slopes,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+    float scale, float k_scale, float v_scale,
+    const uint8_t *pair_mask, int num_threads) {
+    return oracle_dense_attention_blocksparse(
+        out, query, q_dtype, key_cache, value_cache, kv_dtype, block_tables, max_blocks_per_seq,
+        seq_lens, alibi_slopes, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+        scale, k_scale, v_scale, 0, 0, 0, 1, 0, pair_mask, num_threads);
 }
 
 /* ---- KV-cache write ----------------------------------------------------
