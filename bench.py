@@ -195,6 +195,12 @@ def cache_write_bench(args, dev):
     return result
 
 
+# Block-sparse decode benchmark pattern on the long-context workload:
+# (tp_rank, local_blocks, vert_stride, sparse block size, head sliding step)
+# -- 64-token sparse blocks, the last 16 of them (1024 tokens) as the local
+# window, and every 8th block, the same stripes for every head.
+BLOCKSPARSE_PATTERN = (0, 16, 8, 64, 0)
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFIX_CASE = dict(ctx=[16384] * 4, ql=[512] * 4, H=24, KVH=4, d=256, bs=16, dtype="bf16", seed=1006)
 

@@ -56,6 +56,8 @@ def load():
         L.pav2_paged_attention_v2.restype = I
         L.pav2_paged_attention_v1.argtypes = [P, P, P, P, I, F, P, P, I, I, P, I, F, F, I, I, I, I, I, I, P]
         L.pav2_paged_attention_v1.restype = I
+        L.pav2_paged_attention_v2_blocksparse.argtypes = attn[:17] + [I, I, I, I, I] + attn[17:]
+        L.pav2_paged_attention_v2_blocksparse.restype = I
         L.pav2_paged_attention_v2_noalloc.argtypes = [P, P, P, P, I, F, P, P, I, I, P, I, F, F, I, I, I, I, I, I, P]
         L.pav2_paged_attention_v2_noalloc.restype = I
         L.pav2_noalloc_scratch_bytes.argtypes = []
@@ -169,6 +171,30 @@ def paged_attention_v2(output, exp_sums, max_logits, tmp_output, query, key_cach
         _dev(value_cache, "value_cache"), int(num_kv_heads), float(scale),
         _i32(block_tables, "block_tables"), _i32(seq_lens, "seq_lens"), int(block_size),
         int(max_seq_len), _dev(alibi_slopes, "alibi_slopes"), kvdt, float(k_scale), float(v_scale),
+        S, H, D, int(key_cache.shape[0]), int(block_tables.shape[1]), int(tmp_output.shape[2]),
+        _dtype_code(query), _stream(query, stream))
+    _check(rc)
+
+
+def paged_attention_v2_blocksparse(output, exp_sums, max_logits, tmp_output, query, key_cache, value_cache,
+                                   num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                                   alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
+                                   tp_rank=0, blocksparse_local_blocks=0, blocksparse_vert_stride=0,
+                                   blocksparse_block_size=64, blocksparse_head_sliding_step=0,
+                                   stream=None) -> None:
+    """The pages' V2 op with its block-sparse arguments (the pages' defaults;
+    blocksparse_vert_stride <= 1 is the dense call)."""
+    L = load()
+    S, H, D, kvdt = _common(query, key_cache, value_cache, num_kv_heads, block_tables, seq_lens,
+                            block_size, kv_cache_dtype, alibi_slopes)
+    rc = L.pav2_paged_attention_v2_blocksparse(
+        _dev(output, "output"), _dev(exp_sums, "exp_sums"), _dev(max_logits, "max_logits"),
+        _dev(tmp_output, "tmp_output"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), int(num_kv_heads), float(scale),
+        _i32(block_tables, "block_tables"), _i32(seq_lens, "seq_lens"), int(block_size),
+        int(max_seq_len), _dev(alibi_slopes, "alibi_slopes"), kvdt, float(k_scale), float(v_scale),
+        int(tp_rank), int(blocksparse_local_blocks), int(blocksparse_vert_stride or 0),
+        int(blocksparse_block_size), int(blocksparse_head_sliding_step),
         S, H, D, int(key_cache.shape[0]), int(block_tables.shape[1]), int(tmp_output.shape[2]),
         _dtype_code(query), _stream(query, stream))
     _check(rc)

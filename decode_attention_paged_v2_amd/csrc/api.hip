@@ -143,13 +143,44 @@ int launch_status(hipError_t e, const char *what) {
     return fail(PAV2_ERR_LAUNCH, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
+// The block-sparse arguments of the V2 op (vert_stride <= 1: dense).
+struct Sparse {
+    int tp_rank, local_blocks, vert_stride, block_size, sliding_step;
+};
+
+int check_sparse(const Sparse &sp, const Shape &sh) {
+    if (sp.vert_stride <= 1) return PAV2_OK;
+    if (sp.block_size <= 0 || sp.block_size % sh.block_size)
+        return fail(PAV2_ERR_INVALID_ARGUMENT,
+                    "blocksparse_block_size %d must be a positive multiple of block_size %d", sp.block_size,
+                    sh.block_size);
+    if (sp.local_blocks < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "blocksparse_local_blocks must be >= 0");
+    if (sp.tp_rank < 0) return fail(PAV2_ERR_INVALID_ARGUMENT, "tp_rank must be >= 0");
+    if (sp.block_size > (1 << 24) || ((int64_t)sp.tp_rank + 1) * sh.num_heads > ((int64_t)1 << 30))
+        return fail(PAV2_ERR_UNSUPPORTED, "blocksparse_block_size %d or tp_rank %d too large", sp.block_size,
+                    sp.tp_rank);
+    return PAV2_OK;
+}
+
 int run_phase1(float *exp_sums, float *max_logits, void *tmp_output, const void *query,
                const void *key_cache, const void *value_cache, float scale,
                const int32_t *block_tables, const int32_t *seq_lens, const float *alibi_slopes,
-               float k_scale, float v_scale, const Shape &sh, hipStream_t stream) {
+               float k_scale, float v_scale, const Shape &sh, hipStream_t stream,
+               const Sparse *sparse = nullptr) {
     pav2_plan_t pl;
     make_plan(sh, &pl);
     pav2::Phase1Params p;
+    const bool sp = sparse != nullptr && sparse->vert_stride > 1;
+    if (sp) {
+        p.tp_rank = sparse->tp_rank;
+        p.sp_local_blocks = sparse->local_blocks;
+        p.sp_vert_stride = sparse->vert_stride;
+        p.sp_block_size = sparse->block_size;
+        p.sp_sliding_step = sparse->sliding_step;
+        pl.phase1_lds_bytes = pav2::phase1_lds_bytes(sh.num_heads / sh.num_kv_heads, sh.head_size, pav2::kPhase1Waves,
+                                                     ilog2_exact(sh.block_size), sh.num_seqs, pl.phase1_compact != 0,
+                                                     true);
+    }
     p.tmp_out = tmp_output;
     p.exp_sums = exp_sums;
     p.max_logits = max_logits;
@@ -356,6 +387,38 @@ int pav2_paged_attention_v2(void *output, float *exp_sums, float *max_logits, vo
     hipStream_t st = static_cast<hipStream_t>(stream);
     rc = run_phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, scale,
                     block_tables, seq_lens, alibi_slopes, k_scale, v_scale, sh, st);
+    if (rc) return rc;
+    return run_phase2(output, exp_sums, max_logits, tmp_output, seq_lens, num_seqs, num_heads,
+                      head_size, max_num_partitions, (int)query_dtype, st);
+}
+
+int pav2_paged_attention_v2_blocksparse(void *output, float *exp_sums, float *max_logits, void *tmp_output,
+                                        const void *query, const void *key_cache, const void *value_cache,
+                                        int num_kv_heads, float scale, const int32_t *block_tables,
+                                        const int32_t *seq_lens, int block_size, int max_seq_len,
+                                        const float *alibi_slopes, pav2_dtype_t kv_cache_dtype, float k_scale,
+                                        float v_scale, int tp_rank, int blocksparse_local_blocks,
+                                        int blocksparse_vert_stride, int blocksparse_block_size,
+                                        int blocksparse_head_sliding_step, int num_seqs, int num_heads,
+                                        int head_size, int num_blocks, int max_blocks_per_seq,
+                                        int max_num_partitions, pav2_dtype_t query_dtype, pav2_stream_t stream) {
+    g_err[0] = 0;
+    Shape sh{num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks,
+             max_blocks_per_seq, max_num_partitions, max_seq_len, (int)query_dtype, (int)kv_cache_dtype};
+    int rc = check_shape(sh);
+    if (rc) return rc;
+    const Sparse sp{tp_rank, blocksparse_local_blocks, blocksparse_vert_stride, blocksparse_block_size,
+                    blocksparse_head_sliding_step};
+    rc = check_sparse(sp, sh);
+    if (rc) return rc;
+    if (num_seqs == 0) return PAV2_OK;
+    if (!output) return fail(PAV2_ERR_INVALID_ARGUMENT, "output is NULL");
+    rc = check_phase1_args(exp_sums, max_logits, tmp_output, query, key_cache, value_cache,
+                           block_tables, seq_lens, scale, k_scale, v_scale);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = run_phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, scale,
+                    block_tables, seq_lens, alibi_slopes, k_scale, v_scale, sh, st, &sp);
     if (rc) return rc;
     return run_phase2(output, exp_sums, max_logits, tmp_output, seq_lens, num_seqs, num_heads,
                       head_size, max_num_partitions, (int)query_dtype, st);

@@ -57,6 +57,11 @@ struct Phase1Params {
     int64_t head_stride;           // bytes per (block, kv head)
     float scale_log2;              // scale * k_scale * log2(e)
     float v_scale;
+    // block-sparse pattern (sp_vert_stride > 1; the dense kernels ignore it):
+    // head h (model-wide index tp_rank * num_heads + h) attends token t when
+    // t / sp_block_size > (L - 1) / sp_block_size - sp_local_blocks or
+    // (t / sp_block_size - h' * sp_sliding_step) mod sp_vert_stride == 0
+    int tp_rank = 0, sp_local_blocks = 0, sp_vert_stride = 0, sp_block_size = 1, sp_sliding_step = 0;
 };
 
 struct Phase2Params {
@@ -148,14 +153,16 @@ inline bool prefer_single_pass(int64_t seq_items, int max_num_partitions) {
            max_num_partitions <= kSinglePassMaxPartitions;
 }
 
-inline int phase1_lds_bytes(int gqa, int head_size, int waves, int bs_log2, int num_seqs, bool compact) {
+inline int phase1_lds_bytes(int gqa, int head_size, int waves, int bs_log2, int num_seqs, bool compact,
+                            bool sparse = false) {
     int heads = gqa < kMaxHeadsPerGroup ? gqa : kMaxHeadsPerGroup;
     int d16 = (head_size + 15) / 16 * 16;
     int table = (kPartition >> bs_log2) * 4;
     return waves * heads * (d16 + 4) * 4      // per-wave partial outputs
            + 3 * waves * kMaxHeadsPerGroup * 4 // per-wave max and sums
            + table                             // the partition's block-table slice
-           + (compact ? (num_seqs + 1 + waves) * 4 : 0);   // partition-count prefix
+           + (num_seqs + 1 + waves) * 4 * (compact ? 1 : 0)   // partition-count prefix
+           + (sparse ? (kMaxHeadsPerGroup + waves) * 4 : 0);   // heads' stripe residues, unit masks
 }
 
 inline int phase2_vec(int odt) { return odt == F32 ? 4 : 8; }

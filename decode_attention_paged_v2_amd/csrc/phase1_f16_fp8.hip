@@ -6,7 +6,7 @@
 namespace pav2 {
 
 hipError_t launch_phase1_f16_fp8(const Phase1Params &p, int head_size, int lds_bytes, hipStream_t stream) {
-    return launch_d<F16, FP8>(p, head_size, lds_bytes, stream);
+    return launch_d<F16, FP8, false>(p, head_size, lds_bytes, stream);
 }
 
 }  // namespace pav2

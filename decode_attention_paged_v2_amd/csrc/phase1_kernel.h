@@ -45,6 +45,8 @@
 //   shifted back to the absolute frame the pages use.
 #include <math.h>
 
+#include <atomic>
+
 #include "pav2_internal.h"
 
 namespace pav2 {
@@ -156,7 +158,10 @@ __device__ __forceinline__ T load_stream(const uint8_t *p) {
 // of the sequence's partitions and writes the final output).
 // BS: the block size when fixed at compile time (16 or 32), 0 for any of
 // 8 .. 512, -1 for 1, 2 or 4 (a lane's 8-token V slice then spans blocks).
-template <int QDT, int KVDT, int D, int WAVES, int SCHED, int BS>
+// SPARSE: the block-sparse pattern of Phase1Params (dense and compact
+// schedules only): units of a partition that no head of the group attends
+// are never loaded, and scores of tokens a head does not attend are masked.
+template <int QDT, int KVDT, int D, int WAVES, int SCHED, int BS, bool SPARSE>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(kPhase1Occupancy)))
 phase1_kernel(const Phase1Params P) {
     constexpr bool COMPACT = SCHED == 1;
@@ -193,6 +198,8 @@ phase1_kernel(const Phase1Params P) {
     int *s_bt = reinterpret_cast<int *>(s_lr + WAVES * kMaxHeadsPerGroup);
     int *s_pref = s_bt + (kPartition >> bs_log2);       // [num_seqs + 1]
     int *s_wsum = s_pref + P.num_seqs + 1;              // [WAVES]
+    // block-sparse: each wavefront's bits of the attended-unit mask
+    uint32_t *s_umask = reinterpret_cast<uint32_t *>(COMPACT ? s_wsum + WAVES : s_pref);   // [WAVES]
 
     // Work items.  Dense schedule: one (partition, seq, kv head, head group)
     // slot per workgroup, consecutive slots on one XCD (blockIdx.x % 8).
@@ -409,7 +416,52 @@ phase1_kernel(const Phase1Params P) {
     if (P.alibi != nullptr && hvalid) slope2 = P.alibi[h0 + col] * kLog2e;
     const float scale_log2 = P.scale_log2;
 
-    __syncthreads();   // block-table slice ready
+    // Block-sparse: sparse blocks above sp_klo are the local window; this
+    // lane's head attends the stripe residue sp_res (mod vert_stride).  Each
+    // thread tests kPartition / (WAVES * 64) consecutive tokens against every
+    // head of the group, and a ballot gives each wavefront's 32-token units
+    // their "attended by some head" bits.
+    int sp_res = -1, sp_klo = 0;
+    if constexpr (SPARSE) {
+        const int vs = P.sp_vert_stride, B = P.sp_block_size;
+        sp_klo = (L - 1) / B - P.sp_local_blocks;
+        if (hvalid) {
+            const int64_t x = (int64_t)(P.tp_rank * P.num_heads + h0 + col) * P.sp_sliding_step;
+            const int r = (int)(x % vs);
+            sp_res = r < 0 ? r + vs : r;
+        }
+        int rall[kMaxHeadsPerGroup];   // every head's residue (lane c holds head c's)
+#pragma unroll
+        for (int c = 0; c < kMaxHeadsPerGroup; ++c) rall[c] = __shfl(sp_res, c);
+        constexpr int TPT = kPartition / (WAVES * 64);   // tokens per thread
+        constexpr int TPU = 32 / TPT;                    // threads per 32-token unit
+        static_assert(kPartition % (WAVES * 64) == 0 && TPU >= 1 && TPU <= 64, "unit test layout");
+        bool hit = false;
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int t = start + tid * TPT + k;
+            if (t < L) {
+                const int kb = t / B;
+                if (kb > sp_klo) {
+                    hit = true;
+                } else {
+                    const int r = kb % vs;
+#pragma unroll
+                    for (int c = 0; c < kMaxHeadsPerGroup; ++c) hit = hit || (c < nh && rall[c] == r);
+                }
+            }
+        }
+        const uint64_t bal = __ballot(hit);
+        if (lane == 0) {
+            uint32_t bits = 0;
+#pragma unroll
+            for (int j = 0; j < 64 / TPU; ++j)
+                if ((bal >> (j * TPU)) & (TPU == 64 ? ~0ull : ((1ull << TPU) - 1))) bits |= 1u << j;
+            s_umask[wv] = bits << (wv * (64 / TPU));
+        }
+    }
+
+    __syncthreads();   // block-table slice ready (and the attended-unit bits)
 
     const uint8_t *kc = P.key_cache + (int64_t)g * P.head_stride;
     const uint8_t *vc = P.value_cache + (int64_t)g * P.head_stride;
@@ -421,9 +473,29 @@ phase1_kernel(const Phase1Params P) {
     constexpr int UNIT = 32;
     constexpr int UPW = PREFIX ? kPrefixSlice / UNIT : (kPartition / UNIT) / WAVES;   // units per wavefront
     const int nunits = (n_tok + UNIT - 1) / UNIT;
+    // Block-sparse: the wavefronts deal out the list of attended units
+    // (ascending) round-robin; entries past the list's end are -1.
+    int sp_unit[SPARSE ? UPW : 1];
+    if constexpr (SPARSE) {
+        uint32_t um = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < WAVES; ++w2) um |= s_umask[w2];
+        um = __builtin_amdgcn_readfirstlane(um);
+        for (int i = 0; i < wv; ++i) um &= um - 1;   // skip the first wv attended units
+#pragma unroll
+        for (int u = 0; u < UPW; ++u) {
+            sp_unit[u] = um ? __builtin_ctz(um) : -1;
+            for (int i = 0; i < WAVES; ++i) um &= um - 1;
+        }
+    }
     auto unit_of = [&](int u) {
         if constexpr (PREFIX) return (item % (kPartition / kPrefixSlice)) * UPW + u;
+        else if constexpr (SPARSE) return sp_unit[u];
         else return wv + WAVES * u;
+    };
+    auto uvalid = [&](int u) {
+        if constexpr (SPARSE) return sp_unit[u] >= 0;
+        else return true;
     };
     auto clamp_unit = [&](int t) { return t < nunits ? t : 0; };
 
@@ -580,10 +652,12 @@ phase1_kernel(const Phase1Params P) {
 
     auto issue = [&](int j) {
         if (j < GK) {
+            if (uvalid(j / KG)) {
 #pragma unroll
-            for (int hh = 0; hh < KH; ++hh) load_k(kbuf[j % PF][hh], j / KG, (j % KG) * KH + hh);
+                for (int hh = 0; hh < KH; ++hh) load_k(kbuf[j % PF][hh], j / KG, (j % KG) * KH + hh);
+            }
         } else if (j < NG) {
-            load_v(vbuf[j % PF], (j - GK) / VSPLIT, (j - GK) % VSPLIT);
+            if (uvalid((j - GK) / VSPLIT)) load_v(vbuf[j % PF], (j - GK) / VSPLIT, (j - GK) % VSPLIT);
         }
     };
 
@@ -597,7 +671,7 @@ phase1_kernel(const Phase1Params P) {
         const int u = j / KG;
         f32x4 acc[KH];
 #pragma unroll
-        for (int hh = 0; hh < KH; ++hh) acc[hh] = qk_tile(kbuf[j % PF][hh]);
+        for (int hh = 0; hh < KH; ++hh) acc[hh] = uvalid(u) ? qk_tile(kbuf[j % PF][hh]) : f32x4{0.f, 0.f, 0.f, 0.f};
         issue(j + PF);
 #pragma unroll
         for (int hh = 0; hh < KH; ++hh) {
@@ -623,7 +697,8 @@ phase1_kernel(const Phase1Params P) {
             sc[u][i] = as_f32(q[0]);
             sc[u][4 + i] = as_f32(q[1]);
         }
-        const float bu = u == 0 ? bias0 : fmaf(slope2, (float)(WAVES * UNIT * u), bias0);
+        float bu = u == 0 ? bias0 : fmaf(slope2, (float)(WAVES * UNIT * u), bias0);
+        if constexpr (SPARSE) bu = slope2 * (float)(start + unit_of(u) * UNIT + 8 * grp - last);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             sc[u][e] = fmaf(sc[u][e], scale_log2, e == 0 ? bu : fmaf(slope2, (float)e, bu));
@@ -632,6 +707,25 @@ phase1_kernel(const Phase1Params P) {
             const int nv = lcol - (tu + 8 * grp);   // valid tokens among the lane's 8
 #pragma unroll
             for (int e = 0; e < 8; ++e) sc[u][e] = e < nv ? sc[u][e] : -INFINITY;
+        }
+        if constexpr (SPARSE) {
+            const int B = P.sp_block_size, vs = P.sp_vert_stride;
+            if (!uvalid(u)) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sc[u][e] = -INFINITY;
+            } else if (tu / B <= sp_klo) {   // not wholly inside the local window: test each token
+                const int t0 = tu + 8 * grp;
+                int kb = t0 / B, nb = (kb + 1) * B, r = kb % vs;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (t0 + e >= nb) {   // next sparse block (B >= 1: at most one step per token)
+                        ++kb;
+                        nb += B;
+                        r = r + 1 == vs ? 0 : r + 1;
+                    }
+                    sc[u][e] = (kb > sp_klo || r == sp_res) ? sc[u][e] : -INFINITY;
+                }
+            }
         }
     }
 
@@ -678,6 +772,10 @@ phase1_kernel(const Phase1Params P) {
     for (int j = GK; j < NG; ++j) {
         const int u = (j - GK) / VSPLIT;
         const int part = (j - GK) % VSPLIT;
+        if (!uvalid(u)) {   // block-sparse: nothing loaded, no weight
+            issue(j + PF);
+            continue;
+        }
         if (part == 0) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -834,7 +932,9 @@ phase1_kernel(const Phase1Params P) {
         const int d0 = (idx - hh * PER_HEAD) * VEC;
         float M, l, lr, r[VEC];
         combine(hh, d0, M, l, lr, r);
-        const float inv = v_scale / lr;
+        // block-sparse: a head may attend no token of the partition (l = 0):
+        // its row is zero and its statistics -inf / 0, weight 0 in phase 2
+        const float inv = SPARSE ? (lr > 0.0f ? v_scale / lr : 0.0f) : v_scale / lr;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) r[e] *= inv;
         const int h = h0 + hh;
@@ -926,40 +1026,74 @@ phase1_kernel(const Phase1Params P) {
     }
 }
 
-int device_cu_count() {
-    static int cache[64] = {0};
+constexpr int kMaxDevices = 64;
+
+int current_device() {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    return dev;
 }
 
-template <int QDT, int KVDT, int D, int SCHED, int BS>
+int device_cu_count(int dev) {
+    static std::atomic<int> cache[kMaxDevices];
+    if (dev < 0) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Host state of one kernel variant, per device: the largest dynamic LDS size
+// it has been allowed, and its resident workgroups per CU at the last LDS
+// size asked for (packed (lds << 32) | workgroups in one atomic word), so a
+// launch queries the runtime only when the LDS size changes.
+struct VariantState {
+    std::atomic<int> lds_allowed[kMaxDevices];
+    std::atomic<uint64_t> occupancy[kMaxDevices];
+};
+
+hipError_t allow_lds(VariantState &st, const void *fn, int dev, int lds) {
+    if (lds <= 65536) return hipSuccess;
+    if (dev >= 0 && st.lds_allowed[dev].load(std::memory_order_relaxed) >= lds) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess && dev >= 0) st.lds_allowed[dev].store(lds, std::memory_order_relaxed);
+    return e;
+}
+
+int resident_per_cu(VariantState &st, const void *fn, int dev, int threads, int lds) {
+    if (dev >= 0) {
+        const uint64_t c = st.occupancy[dev].load(std::memory_order_relaxed);
+        if (c != 0 && (int)(c >> 32) == lds) return (int)(c & 0xffffffffu);
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess || per_cu <= 0)
+        per_cu = 1;
+    if (dev >= 0) st.occupancy[dev].store(((uint64_t)(uint32_t)lds << 32) | (uint32_t)per_cu, std::memory_order_relaxed);
+    return per_cu;
+}
+
+template <int QDT, int KVDT, int D, int SCHED, int BS, bool SPARSE>
 hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
     constexpr int WAVES = kPhase1Waves;
-    const void *fn = reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, SCHED, BS>);
-    if (lds > 65536) hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    static VariantState state;
+    const void *fn = reinterpret_cast<const void *>(&phase1_kernel<QDT, KVDT, D, WAVES, SCHED, BS, SPARSE>);
+    const int dev = current_device();
+    const hipError_t e = allow_lds(state, fn, dev, lds);
+    if (e != hipSuccess) return e;
     int grid = (p.num_work + 7) / 8 * 8;
     if (SCHED == 1) {
         // at most kPhase1CompactRounds resident rounds of workgroups, each
         // walking a balanced range of the used items
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, WAVES * 64, lds) != hipSuccess ||
-            per_cu <= 0)
-            per_cu = 1;
-        const int cap = kPhase1CompactRounds * device_cu_count() * per_cu;
+        const int cap = kPhase1CompactRounds * device_cu_count(dev) * resident_per_cu(state, fn, dev, WAVES * 64, lds);
         grid = grid < cap ? grid : cap;
     } else if (SCHED == 2) {
         grid = p.num_work;   // one workgroup per (sequence, kv head, head group)
     } else if (SCHED == 3) {
         grid = (p.num_work + 7) / 8 * 8;   // one per (sequence, kv head, row block), a multiple of 8
     }
-    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, SCHED, BS>), dim3(grid), dim3(WAVES * 64), lds,
+    hipLaunchKernelGGL((phase1_kernel<QDT, KVDT, D, WAVES, SCHED, BS, SPARSE>), dim3(grid), dim3(WAVES * 64), lds,
                        stream, p);
     return hipGetLastError();
 }
@@ -969,41 +1103,49 @@ hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
 // 16-token K tile, and at 32 of a whole unit, is wave-uniform); blocks of 1,
 // 2 or 4 tokens a kernel whose V gather takes each token from its own block
 // (BS = -1); every other case runs the generic kernel.
-template <int QDT, int KVDT, int D, int SCHED>
+template <int QDT, int KVDT, int D, int SCHED, bool SPARSE>
 hipError_t launch_bs(const Phase1Params &p, int lds, hipStream_t stream) {
-    if (p.bs_log2 < 3) return launch_sched<QDT, KVDT, D, SCHED, -1>(p, lds, stream);   // blocks of 1, 2, 4
-    if constexpr (QDT != F32) {
-        if (p.bs_log2 == 4) return launch_sched<QDT, KVDT, D, SCHED, 16>(p, lds, stream);
-        if (p.bs_log2 == 5) return launch_sched<QDT, KVDT, D, SCHED, 32>(p, lds, stream);
+    if (p.bs_log2 < 3) return launch_sched<QDT, KVDT, D, SCHED, -1, SPARSE>(p, lds, stream);   // blocks of 1, 2, 4
+    if constexpr (QDT != F32 && !SPARSE) {
+        if (p.bs_log2 == 4) return launch_sched<QDT, KVDT, D, SCHED, 16, false>(p, lds, stream);
+        if (p.bs_log2 == 5) return launch_sched<QDT, KVDT, D, SCHED, 32, false>(p, lds, stream);
     }
-    return launch_sched<QDT, KVDT, D, SCHED, 0>(p, lds, stream);
+    return launch_sched<QDT, KVDT, D, SCHED, 0, SPARSE>(p, lds, stream);
 }
 
-template <int QDT, int KVDT, int D>
+template <int QDT, int KVDT, int D, bool SPARSE>
 hipError_t launch_one(const Phase1Params &p, int lds, hipStream_t stream) {
-    switch (p.sched) {
-    case 0: return launch_bs<QDT, KVDT, D, 0>(p, lds, stream);
-    case 1: return launch_bs<QDT, KVDT, D, 1>(p, lds, stream);
-    case 2: return launch_bs<QDT, KVDT, D, 2>(p, lds, stream);
-    case 3:
-        if constexpr (QDT == KVDT) return launch_bs<QDT, KVDT, D, 3>(p, lds, stream);   // 16/32-bit caches
-        else return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+    if constexpr (SPARSE) {   // block-sparse: the two-phase schedules only
+        switch (p.sched) {
+        case 0: return launch_bs<QDT, KVDT, D, 0, true>(p, lds, stream);
+        case 1: return launch_bs<QDT, KVDT, D, 1, true>(p, lds, stream);
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (p.sched) {
+        case 0: return launch_bs<QDT, KVDT, D, 0, false>(p, lds, stream);
+        case 1: return launch_bs<QDT, KVDT, D, 1, false>(p, lds, stream);
+        case 2: return launch_bs<QDT, KVDT, D, 2, false>(p, lds, stream);
+        case 3:
+            if constexpr (QDT == KVDT) return launch_bs<QDT, KVDT, D, 3, false>(p, lds, stream);   // 16/32-bit caches
+            else return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+        }
     }
 }
 
-template <int QDT, int KVDT>
+template <int QDT, int KVDT, bool SPARSE>
 hipError_t launch_d(const Phase1Params &p, int D, int lds, hipStream_t stream) {
     switch (D) {
-    case 64: return launch_one<QDT, KVDT, 64>(p, lds, stream);
-    case 80: return launch_one<QDT, KVDT, 80>(p, lds, stream);
-    case 96: return launch_one<QDT, KVDT, 96>(p, lds, stream);
-    case 112: return launch_one<QDT, KVDT, 112>(p, lds, stream);
-    case 128: return launch_one<QDT, KVDT, 128>(p, lds, stream);
-    case 192: return launch_one<QDT, KVDT, 192>(p, lds, stream);
-    case 256: return launch_one<QDT, KVDT, 256>(p, lds, stream);
+    case 64: return launch_one<QDT, KVDT, 64, SPARSE>(p, lds, stream);
+    case 80: return launch_one<QDT, KVDT, 80, SPARSE>(p, lds, stream);
+    case 96: return launch_one<QDT, KVDT, 96, SPARSE>(p, lds, stream);
+    case 112: return launch_one<QDT, KVDT, 112, SPARSE>(p, lds, stream);
+    case 128: return launch_one<QDT, KVDT, 128, SPARSE>(p, lds, stream);
+    case 192: return launch_one<QDT, KVDT, 192, SPARSE>(p, lds, stream);
+    case 256: return launch_one<QDT, KVDT, 256, SPARSE>(p, lds, stream);
     case 120:
-        if constexpr (KVDT != FP8) return launch_one<QDT, KVDT, 120>(p, lds, stream);
+        if constexpr (KVDT != FP8) return launch_one<QDT, KVDT, 120, SPARSE>(p, lds, stream);
         else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }

@@ -214,7 +214,9 @@ __global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const 
         }
     }
     if (gi == 0) {
-        const float inv = 1.0f / w;
+        // w == 0: every partition empty (block-sparse heads that attend
+        // no token): a zero row, as for an empty sequence
+        const float inv = w > 0.0f ? 1.0f / w : 0.0f;
         float o[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) o[e] = acc[e] * inv;

@@ -114,6 +114,46 @@ int pav2_paged_attention_v2(
     pav2_stream_t stream);
 
 /*
+ * Block-sparse PagedAttention V2: pav2_paged_attention_v2 with the V2 op's
+ * remaining arguments, tp_rank and the four blocksparse_* ones, in the pages'
+ * order (page "paged_attention_v2_pytorch.py", the op's signature; page
+ * "paged_attn.py", forward_decode, which takes the block-sparse branch when
+ * blocksparse_vert_stride > 1 and asserts that blocksparse_block_size is a
+ * multiple of block_size).  The pages give no body; the pattern taken from
+ * the names: with B = blocksparse_block_size, key token t lies in sparse
+ * block k = t / B and the decode query (position L - 1) in q = (L - 1) / B;
+ * query head h, whose index in the whole model is h' = tp_rank * num_heads +
+ * h, attends token t < L when
+ *     k > q - blocksparse_local_blocks                     (local window), or
+ *     (k - h' * blocksparse_head_sliding_step) mod blocksparse_vert_stride == 0
+ *                                       (vertical stripes, slid per head).
+ * Tokens a head does not attend take no part in its softmax; a partition in
+ * which a head attends nothing gets max_logits = -inf, exp_sums = 0 and a
+ * zero tmp_output row; a head that attends nothing at all gets a zero output
+ * row.  32-token spans that no head of a kv head's group attends are never
+ * read.  blocksparse_vert_stride <= 1 is the dense call (the other sparse
+ * arguments are then ignored).
+ *
+ * Errors as pav2_paged_attention_v2, plus PAV2_ERR_INVALID_ARGUMENT for
+ * blocksparse_block_size not a positive multiple of block_size, a negative
+ * blocksparse_local_blocks or tp_rank (when vert_stride > 1).
+ */
+int pav2_paged_attention_v2_blocksparse(
+    void *output, float *exp_sums, float *max_logits, void *tmp_output,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_kv_heads, float scale,
+    const int32_t *block_tables, const int32_t *seq_lens,
+    int block_size, int max_seq_len,
+    const float *alibi_slopes,
+    pav2_dtype_t kv_cache_dtype, float k_scale, float v_scale,
+    int tp_rank, int blocksparse_local_blocks, int blocksparse_vert_stride,
+    int blocksparse_block_size, int blocksparse_head_sliding_step,
+    int num_seqs, int num_heads, int head_size, int num_blocks,
+    int max_blocks_per_seq, int max_num_partitions,
+    pav2_dtype_t query_dtype,
+    pav2_stream_t stream);
+
+/*
  * PagedAttention V1, the single-pass variant (page "paged_attn.py",
  * forward_decode, which calls it when every sequence fits one partition or
  * when the sequence x head parallelism already fills the device): the same
