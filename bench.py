@@ -5,19 +5,28 @@ A step is one pass of the whole hot path over one batch: phase 1 (the
 per-partition kernel) and phase 2 (the log-sum-exp combine), launched through
 the C ABI on the current stream, on synthetic inputs already resident in HBM.
 
-Default workload: 4 sequences x 100000 tokens, 24 query heads over 4 kv heads
-(GQA 6), head size 256, bf16, block size 16 -- the long-context GQA decode the
-metric names.  `--config` selects one of the other workloads.  `--entry v1`
-times the single-pass entry point instead (one launch per step), `--entry
-auto` whichever of the two the library's planner picks for the workload.
+Timing: before every timed step a read sweep of 1 GiB with ordinary loads
+evicts L2 and the 256 MB Infinity Cache (without leaving dirty lines behind);
+a HIP event pair on the launch stream brackets phase 1 + phase 2 of the step.
+`ms_per_step` is the median of those steps (min and mean reported too);
+phase 1's own duration comes from a second pass of flushed steps with an
+event between the two kernels.  A warm pass (back-to-back steps, host wall
+clock) is reported as a secondary figure.
+
+Default run: the long-context GQA decode the metric names (4 sequences x
+100000 tokens, 24 query heads over 4 kv heads, head size 256, bf16, block
+size 16) as the headline; a `configs` map with the same measurement for all
+five workloads (step times, KV GB/s, % of 8 TB/s, and the error of sampled
+(sequence, head) outputs against the float64 oracle); the block-sparse
+decode of the long-context workload (attended bytes only); the chip's
+achievable read bandwidth (a plain non-temporal read stream); and the CPU
+oracle baseline.  `--config` selects another headline workload, `--single`
+measures that workload alone, `--entry v1 | auto` times the single-pass entry
+point or the planner's choice.
 
 Prints ONE JSON line.  `value` is KV bytes read per second (decimal GB/s);
 `roofline` reports phase 1's algorithmic bytes per launch over its mean
-duration (HIP events on the launch stream, inside the timed region, on every
-fifth step) against
-MI355X's 8 TB/s HBM peak; `cpu_baseline` times the float64 CPU oracle on a
-bounded sample of the same workload and also checks those outputs against the
-GPU's.
+flushed duration against MI355X's 8 TB/s HBM peak.
 """
 from __future__ import annotations
 
@@ -31,7 +40,9 @@ import numpy as np
 import torch
 
 HBM_PEAK_GBPS = 8000.0
-EVENT_EVERY = 5      # timed steps per phase-1 event pair
+FLUSH_BYTES = 1 << 30          # read sweep between timed steps (> L2 + Infinity Cache)
+STREAM_BYTES = 4 << 30         # buffer of the achievable-bandwidth read stream
+ORACLE_TOL = {torch.float32: 1e-5, torch.float16: 2e-3, torch.bfloat16: 2e-3}
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -98,7 +109,7 @@ def measured_traffic(config, entry="v2"):
     copy's reading) from the committed counter summary, or None when there is
     none or it was taken on different kernel sources."""
     from decode_attention_paged_v2_amd import rocprof_harness
-    name = f"phase1_{config}.json" if entry == "v2" else f"v1_{config}.json"
+    name = {"v2": "phase1_", "v1": "v1_", "blocksparse": "blocksparse_"}[entry] + config + ".json"
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -312,6 +323,175 @@ def copy_reference(dev, steps, warmup, nbytes=1 << 30):
             "read_plus_write_GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+class Timer:
+    """Flushed step timing on one stream: a read sweep of FLUSH_BYTES with
+    ordinary loads before each step (outside the events), a HIP event pair
+    around the step, and optionally an event between its two kernels."""
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.stream = torch.cuda.current_stream(dev)
+        self.buf = torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device=dev)
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def flush(self):
+        pav2.read_stream(self.buf[:FLUSH_BYTES // 4], self.sink, nontemporal=False, stream=self.stream)
+
+    def cold(self, first, second=None, steps=20, split=False):
+        """Per-step event times (ms) of first() [+ second()] after a flush; with
+        split, also the times of first() alone and second() alone."""
+        st = self.stream
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            self.flush()
+            e[0].record(st)
+            first()
+            if split:
+                e[1].record(st)
+            if second is not None:
+                second()
+            e[2].record(st)
+        torch.cuda.synchronize()
+        whole = [e[0].elapsed_time(e[2]) for e in ev]
+        if not split:
+            return whole
+        return whole, [e[0].elapsed_time(e[1]) for e in ev], [e[1].elapsed_time(e[2]) for e in ev]
+
+    def warm(self, fn, steps):
+        """Host wall-clock ms per step of back-to-back fn() calls."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    def read_bandwidth(self, reps=10):
+        """The achievable read rate: a non-temporal 16-byte-load stream over STREAM_BYTES."""
+        fn = lambda: pav2.read_stream(self.buf, self.sink, nontemporal=True, stream=self.stream)
+        for _ in range(3):
+            fn()
+        ms = self.cold(fn, steps=reps)
+        best, med = float(np.min(ms)), float(np.median(ms))
+        return {"bytes": STREAM_BYTES, "kernel": "read_stream_kernel (non-temporal 16-byte loads, 4 workgroups / CU)",
+                "ms_median": round(med, 5), "GBps_median": round(STREAM_BYTES / (med * 1e-3) / 1e9, 1),
+                "GBps_best": round(STREAM_BYTES / (best * 1e-3) / 1e9, 1),
+                "pct_of_hbm_peak": round(100 * STREAM_BYTES / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+
+
+def _stats(ms):
+    return {"median": round(float(np.median(ms)), 5), "min": round(float(np.min(ms)), 5),
+            "mean": round(float(np.mean(ms)), 5)}
+
+
+def sample_pairs(wl, n=6, seed=0):
+    """(sequence, head) pairs for the oracle check: the longest sequence's first
+    and last head, an empty sequence if there is one, and random others."""
+    rng = np.random.default_rng(seed)
+    n = min(n, wl.num_seqs * wl.num_heads)
+    lens = wl.seq_lens_host
+    s_max = int(np.argmax(lens))
+    pairs = [(s_max, 0), (s_max, wl.num_heads - 1)]
+    empty = [s for s, L in enumerate(lens) if L == 0]
+    if empty:
+        pairs.append((empty[0], 0))
+    while len(pairs) < n:
+        p = (int(rng.integers(wl.num_seqs)), int(rng.integers(wl.num_heads)))
+        if p not in pairs:
+            pairs.append(p)
+    return pairs
+
+
+def oracle_error(wl, out_gpu, pairs, sparse=None):
+    """Max |gpu - RNE(oracle)| over the pairs' outputs (float64 C oracle, threaded)."""
+    import oracle
+    host = wl.to("cpu")
+    kw = dict(num_kv_heads=wl.num_kv_heads, scale=wl.scale, block_size=wl.block_size,
+              max_num_partitions=wl.max_num_partitions, q_dtype=oracle.dtype_code(wl.q_dtype),
+              kv_dtype=oracle.dtype_code(wl.kv_dtype), alibi_slopes=host.alibi_slopes,
+              k_scale=wl.k_scale, v_scale=wl.v_scale, pairs=pairs, threads=min(16, os.cpu_count() or 1))
+    if sparse is not None:
+        kw.update(tp_rank=sparse[0], blocksparse_local_blocks=sparse[1], blocksparse_vert_stride=sparse[2],
+                  blocksparse_block_size=sparse[3], blocksparse_head_sliding_step=sparse[4])
+    t0 = time.perf_counter()
+    r = oracle.paged_attention_v2(host.query, host.key_cache, host.value_cache, host.block_tables,
+                                  host.seq_lens, **kw)
+    dt = time.perf_counter() - t0
+    err = 0.0
+    for s, h in pairs:
+        ref = torch.from_numpy(r["out"][s, h]).to(wl.q_dtype).double()
+        err = max(err, float((out_gpu[s, h].double() - ref).abs().max()))
+    tol = 1e-2 if wl.kv_dtype == torch.float8_e4m3fn else ORACLE_TOL[wl.q_dtype]
+    return {"pairs": len(pairs), "max_abs_err_vs_rounded_oracle": err, "tolerance": tol, "oracle_s": round(dt, 2)}
+
+
+def measure_decode(name, dev, timer, steps, warmup, entry="v2", sparse=None, check=True):
+    """Flushed and warm step times of one workload (V2 both phases, the single
+    pass, or block-sparse V2), with sampled oracle errors."""
+    spec = W.SPECS[name]
+    t0 = time.time()
+    wl = W.generate(spec, device=dev, poison=False)
+    gen_s = time.time() - t0
+    S, H, D, P = wl.num_seqs, wl.num_heads, wl.head_size, wl.max_num_partitions
+    out = torch.empty_like(wl.query)
+    es = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    ml = torch.empty_like(es)
+    tmp = torch.empty((S, H, P, D), dtype=wl.q_dtype, device=dev)
+    a = (wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale, wl.block_tables,
+         wl.seq_lens, wl.block_size, wl.max_seq_len)
+    kw = dict(alibi_slopes=wl.alibi_slopes, k_scale=wl.k_scale, v_scale=wl.v_scale,
+              kv_cache_dtype="fp8_e4m3" if wl.kv_dtype == torch.float8_e4m3fn else "auto")
+    plan = pav2.plan(S, H, wl.num_kv_heads, D, wl.block_size, P, pav2._binding._dtype_code(wl.query),
+                     pav2._binding._dtype_code(wl.key_cache))
+    if entry == "auto":
+        entry = "v1" if plan["use_v1"] else "v2"
+    if sparse is not None:
+        sk = dict(tp_rank=sparse[0], blocksparse_local_blocks=sparse[1], blocksparse_vert_stride=sparse[2],
+                  blocksparse_block_size=sparse[3], blocksparse_head_sliding_step=sparse[4])
+        first = lambda: pav2.phase1_blocksparse(es, ml, tmp, *a, **kw, **sk)
+        second = lambda: pav2.phase2(out, es, ml, tmp, wl.seq_lens)
+        acct = accounting.blocksparse_workload_bytes(wl, sparse)
+        kv, b1 = acct["kv"], acct["phase1"]
+    elif entry == "v1":
+        first, second = (lambda: pav2.paged_attention_v1(out, *a, **kw)), None
+        acct = accounting.workload_bytes(wl)
+        kv, b1 = acct["kv"], acct["v1"]
+    else:
+        first = lambda: pav2.phase1(es, ml, tmp, *a, **kw)
+        second = lambda: pav2.phase2(out, es, ml, tmp, wl.seq_lens)
+        acct = accounting.workload_bytes(wl)
+        kv, b1 = acct["kv"], acct["phase1"]
+    step = (lambda: (first(), second())) if second is not None else first
+    for _ in range(warmup):
+        timer.flush()
+        step()
+    whole = timer.cold(first, second, steps)
+    res = {"workload": f"{name}: {DESCR[name]}", "entry": "blocksparse" if sparse is not None else entry,
+           "planner_entry": "v1" if plan["use_v1"] else "v2", "generate_s": round(gen_s, 2),
+           "kv_bytes_per_step": kv, "step_ms": _stats(whole)}
+    med = float(np.median(whole))
+    res["kv_GBps"] = round(kv / (med * 1e-3) / 1e9, 2)
+    res["pct_of_hbm_peak"] = round(100.0 * kv / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)
+    res["tokens_heads_per_s"] = round(wl.tokens_heads() / (med * 1e-3), 1)
+    if second is not None:
+        _, p1, p2 = timer.cold(first, second, steps, split=True)
+        res["phase1_ms"] = _stats(p1)
+        res["phase2_ms"] = _stats(p2)
+    elif b1 is not None:
+        res["phase1_ms"] = _stats(whole)     # one launch: the single pass is the step
+    if b1 is not None:
+        res["phase1_algorithmic_bytes"] = b1
+        res["phase1_GBps"] = round(b1 / (res["phase1_ms"]["mean"] * 1e-3) / 1e9, 2)
+    res["warm_ms_per_step"] = round(timer.warm(step, steps), 5)
+    if check:
+        torch.cuda.synchronize()
+        res["oracle_check"] = oracle_error(wl, out.cpu(), sample_pairs(wl), sparse)
+    print(f"[bench] {name}{' block-sparse' if sparse is not None else ''} ({res['entry']}): step median "
+          f"{res['step_ms']['median']:.4f} ms, {res['pct_of_hbm_peak']:.1f} % of 8 TB/s", file=sys.stderr, flush=True)
+    return res, wl, out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,15 +501,15 @@ def main():
     ap.add_argument("--entry", default="v2", choices=["v2", "v1", "auto"],
                     help="v2: both phases (the default); v1: the single-pass entry point; "
                          "auto: the planner's choice")
+    ap.add_argument("--single", action="store_true",
+                    help="measure the --config workload alone (no configs map, block-sparse line or "
+                         "read-stream figure, no oracle check)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--flush-steps", type=int, default=10,
-                    help="extra per-step timings with a 1 GiB cache flush before each step")
-    ap.add_argument("--mode", default="decode", choices=["decode", "copy", "cache_write", "prefix"],
-                    help="copy: time a plain 1 GiB device copy (the reference kernel for "
-                         "scaling HBM byte counters and for achievable bandwidth); cache_write: "
-                         "time the KV-cache write of the workload's whole context (and of one "
-                         "decode step's tokens); prefix: time paged prefix attention for a "
-                         "chunked prefill")
+    ap.add_argument("--mode", default="decode", choices=["decode", "blocksparse", "copy", "cache_write", "prefix"],
+                    help="blocksparse: the block-sparse decode of the workload; copy: time a plain 1 GiB "
+                         "device copy (the reference kernel for scaling HBM byte counters); cache_write: "
+                         "time the KV-cache write of the workload's whole context (and of one decode step's "
+                         "tokens); prefix: time paged prefix attention for a chunked prefill")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -352,118 +532,124 @@ def main():
         print(json.dumps(prefix_bench(args, dev)), flush=True)
         return
     pav2.load()
-    spec = W.SPECS[args.config]
-    t0 = time.time()
-    wl = W.generate(spec, device=dev, poison=False)
-    gen_s = time.time() - t0
+    timer = Timer(dev)
+    if args.mode == "blocksparse":
+        print(json.dumps(blocksparse_line(args, dev, timer)), flush=True)
+        return
 
-    S, H, D, P = wl.num_seqs, wl.num_heads, wl.head_size, wl.max_num_partitions
-    out = torch.empty_like(wl.query)
-    es = torch.empty((S, H, P), dtype=torch.float32, device=dev)
-    ml = torch.empty_like(es)
-    tmp = torch.empty((S, H, P, D), dtype=wl.q_dtype, device=dev)
-    a = (wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale, wl.block_tables,
-         wl.seq_lens, wl.block_size, wl.max_seq_len)
-    kw = dict(alibi_slopes=wl.alibi_slopes, k_scale=wl.k_scale, v_scale=wl.v_scale)
-    stream = torch.cuda.current_stream(dev)
-    plan = pav2.plan(S, H, wl.num_kv_heads, D, wl.block_size, P, pav2._binding._dtype_code(wl.query),
-                     pav2._binding._dtype_code(wl.key_cache))
-    entry = args.entry if args.entry != "auto" else ("v1" if plan["use_v1"] else "v2")
-
-    def step(ev_a=None, ev_b=None, ev_c=None):
-        if ev_a is not None:
-            ev_a.record(stream)
-        if entry == "v1":
-            pav2.paged_attention_v1(out, *a, **kw)
-        else:
-            pav2.phase1(es, ml, tmp, *a, **kw)
-        if ev_b is not None:
-            ev_b.record(stream)
-        if entry == "v2":
-            pav2.phase2(out, es, ml, tmp, wl.seq_lens)
-        if ev_c is not None:
-            ev_c.record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # phase 1's own duration comes from HIP events on every EVENT_EVERY-th step
-    # of the timed region: an event recorded between the two kernels adds a
-    # few microseconds of queue work to its step, so not every step carries one
-    ev = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
-          for i in range(0, args.steps, EVENT_EVERY)}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if i in ev:
-            step(*ev[i])
-        else:
-            step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    p1_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev.values()]
-    p2_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev.values()]
-    ms_per_step = wall * 1e3 / args.steps
-
-    # cold-cache timings: flush L2 and the 256 MB MALL with a 1 GiB write first
-    cold = []
-    if args.flush_steps > 0:
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        for _ in range(args.flush_steps):
-            scratch.fill_(1.0)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            step()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1))
-        del scratch
-
-    kv = wl.kv_bytes()
-    b1 = accounting.workload_bytes(wl)["phase1" if entry == "v2" else "v1"]
+    head, wl, out = measure_decode(args.config, dev, timer, args.steps, args.warmup, args.entry,
+                                   check=not args.single)
+    entry = head["entry"]
+    med = head["step_ms"]["median"]
     traffic = measured_traffic(args.config, entry)
-    p1_mean = float(np.mean(p1_ms))
-    achieved = b1 / (p1_mean * 1e-3) / 1e9
-    value = kv / (ms_per_step * 1e-3) / 1e9
+    b1 = head["phase1_algorithmic_bytes"]
+    achieved = head["phase1_GBps"]
     result = {
         "metric": "decode attention KV GB/s and % of HBM peak (Qwen-style 100K ctx, GQA 6)",
-        "value": round(value, 2),
+        "value": head["kv_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": med,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_NAME[wl.q_dtype] + ("" if wl.kv_dtype == wl.q_dtype else "+fp8_e4m3_kv"),
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: {DESCR[args.config]}", "num_seqs": S,
-                   "num_heads": H, "num_kv_heads": wl.num_kv_heads, "head_size": D,
+        "config": {"workload": head["workload"], "num_seqs": wl.num_seqs,
+                   "num_heads": wl.num_heads, "num_kv_heads": wl.num_kv_heads, "head_size": wl.head_size,
                    "block_size": wl.block_size, "max_seq_len": wl.max_seq_len,
-                   "max_num_partitions": P, "partition_size": 512},
-        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "tokens_heads_per_s": round(wl.tokens_heads() / (ms_per_step * 1e-3), 1),
-        "kv_bytes_per_step": kv,
+                   "max_num_partitions": wl.max_num_partitions, "partition_size": 512},
+        "timing": "median of flushed steps (1 GiB read sweep before each, HIP events around phase 1 + phase 2)",
+        "pct_of_hbm_peak": head["pct_of_hbm_peak"],
+        "tokens_heads_per_s": head["tokens_heads_per_s"],
+        "kv_bytes_per_step": head["kv_bytes_per_step"],
         "entry": entry,
-        "phase1_ms_mean": round(p1_mean, 5),
-        "phase1_event_steps": len(p1_ms),
-        "phase1_ms_min": round(float(np.min(p1_ms)), 5),
-        "phase2_ms_mean": round(float(np.mean(p2_ms)), 5) if entry == "v2" else None,
-        "cold_cache_step_ms_median": round(float(np.median(cold)), 5) if cold else None,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+        "step_ms": head["step_ms"],
+        "phase1_ms": head.get("phase1_ms"),
+        "phase2_ms": head.get("phase2_ms"),
+        "warm_ms_per_step": head["warm_ms_per_step"],
+        "warm_kv_GBps": round(head["kv_bytes_per_step"] / (head["warm_ms_per_step"] * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "kernel": "phase1_kernel" + (" (single pass)" if entry == "v1" else ""),
                      "algorithmic_bytes_per_launch": b1},
-        "generate_s": round(gen_s, 2),
+        "generate_s": head["generate_s"],
         "library": pav2.lib_path(),
     }
+    if "oracle_check" in head:
+        result["oracle_check"] = head["oracle_check"]
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         result["cpu_baseline"] = cpu_baseline(wl, out.cpu())
+        result["cpu_baseline"]["single_thread_tiny"] = single_thread_tiny()
+    del wl, out
+    torch.cuda.empty_cache()
+    if not args.single:
+        result["achievable_read"] = timer.read_bandwidth()
+        configs = {}
+        for name in W.SPECS:
+            if name == args.config:
+                configs[name] = {k: head[k] for k in ("step_ms", "kv_GBps", "pct_of_hbm_peak", "phase1_ms",
+                                                      "phase2_ms", "warm_ms_per_step", "planner_entry",
+                                                      "oracle_check") if k in head}
+                continue
+            r, _, _ = measure_decode(name, dev, timer, args.steps, args.warmup, args.entry)
+            configs[name] = {k: r[k] for k in ("step_ms", "kv_GBps", "pct_of_hbm_peak", "phase1_ms", "phase2_ms",
+                                               "warm_ms_per_step", "planner_entry", "oracle_check") if k in r}
+            torch.cuda.empty_cache()
+        result["configs"] = configs
+        bs, _, _ = measure_decode("long_gqa", dev, timer, args.steps, args.warmup, sparse=BLOCKSPARSE_PATTERN)
+        result["blocksparse"] = {"pattern": dict(zip(("tp_rank", "local_blocks", "vert_stride", "block_size",
+                                                       "head_sliding_step"), BLOCKSPARSE_PATTERN)),
+                                 **{k: bs[k] for k in ("workload", "kv_bytes_per_step", "step_ms", "kv_GBps",
+                                                       "pct_of_hbm_peak", "phase1_ms", "phase1_GBps", "phase2_ms",
+                                                       "warm_ms_per_step", "oracle_check")}}
     print(json.dumps(result), flush=True)
+
+
+def blocksparse_line(args, dev, timer):
+    """Block-sparse V2 on the chosen workload with the benchmark pattern: KV
+    bytes are the attended ones (per kv-head group, the tokens some head attends)."""
+    r, wl, _ = measure_decode(args.config, dev, timer, args.steps, args.warmup, sparse=BLOCKSPARSE_PATTERN,
+                              check=not args.single)
+    med = r["step_ms"]["median"]
+    return {
+        "metric": "block-sparse decode attention: attended KV GB/s and % of HBM peak",
+        "value": r["kv_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": med, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE_NAME[wl.q_dtype], "data": "synthetic",
+        "config": {"workload": r["workload"] + " with 64-token sparse blocks: a 16-block local window and every "
+                                               "8th block, the same stripes for every head",
+                   "pattern": dict(zip(("tp_rank", "local_blocks", "vert_stride", "block_size",
+                                        "head_sliding_step"), BLOCKSPARSE_PATTERN))},
+        "pct_of_hbm_peak": r["pct_of_hbm_peak"], "kv_bytes_per_step": r["kv_bytes_per_step"],
+        "dense_kv_bytes": wl.kv_bytes(), "step_ms": r["step_ms"], "warm_ms_per_step": r["warm_ms_per_step"],
+        "phase1_ms": r["phase1_ms"], "phase2_ms": r["phase2_ms"],
+        "roofline": {"bound": "hbm", "achieved": r["phase1_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(r["phase1_GBps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(args.config, "blocksparse"),
+                     "kernel": "phase1_kernel (block-sparse)",
+                     "algorithmic_bytes_per_launch": r["phase1_algorithmic_bytes"]},
+        **({"oracle_check": r["oracle_check"]} if "oracle_check" in r else {}),
+        "library": pav2.lib_path(),
+    }
+
+
+def single_thread_tiny():
+    """The oracle on the whole tiny workload (1 x 1000 tokens, 4 heads) on one host thread."""
+    import oracle
+    wl = W.generate(W.SPECS["tiny"], poison=False)
+    t0 = time.perf_counter()
+    oracle.paged_attention_v2(wl.query, wl.key_cache, wl.value_cache, wl.block_tables, wl.seq_lens,
+                              num_kv_heads=wl.num_kv_heads, scale=wl.scale, block_size=wl.block_size,
+                              max_num_partitions=wl.max_num_partitions, q_dtype=oracle.F32, kv_dtype=oracle.F32,
+                              threads=1)
+    dt = time.perf_counter() - t0
+    return {"workload": "tiny: " + DESCR["tiny"], "cores": 1, "seconds": round(dt, 4),
+            "GBps": round(wl.kv_bytes() / dt / 1e9, 4), "tokens_heads_per_s": round(wl.tokens_heads() / dt, 1)}
 
 
 if __name__ == "__main__":

@@ -58,6 +58,8 @@ def load():
         L.pav2_paged_attention_v1.restype = I
         L.pav2_paged_attention_v2_blocksparse.argtypes = attn[:17] + [I, I, I, I, I] + attn[17:]
         L.pav2_paged_attention_v2_blocksparse.restype = I
+        L.pav2_phase1_blocksparse.argtypes = attn[1:17] + [I, I, I, I, I] + attn[17:]
+        L.pav2_phase1_blocksparse.restype = I
         L.pav2_paged_attention_v2_noalloc.argtypes = [P, P, P, P, I, F, P, P, I, I, P, I, F, F, I, I, I, I, I, I, P]
         L.pav2_paged_attention_v2_noalloc.restype = I
         L.pav2_noalloc_scratch_bytes.argtypes = []
@@ -74,6 +76,8 @@ def load():
         L.pav2_paged_prefix_attention.restype = I
         L.pav2_reshape_and_cache.argtypes = [P, P, P, P, P, I, F, F, I, I, I, I, I, I, P]
         L.pav2_reshape_and_cache.restype = I
+        L.pav2_read_stream.argtypes = [P, ctypes.c_int64, I, P, P]
+        L.pav2_read_stream.restype = I
         L.pav2_check_inputs.argtypes = [P, P, I, I, I, I, P, P]
         L.pav2_check_inputs.restype = I
         L.pav2_max_num_partitions.argtypes = [I]
@@ -261,6 +265,27 @@ def phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, num_
     _check(rc)
 
 
+def phase1_blocksparse(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, num_kv_heads, scale,
+                       block_tables, seq_lens, block_size, max_seq_len, alibi_slopes=None,
+                       kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0, tp_rank=0, blocksparse_local_blocks=0,
+                       blocksparse_vert_stride=0, blocksparse_block_size=64, blocksparse_head_sliding_step=0,
+                       stream=None) -> None:
+    L = load()
+    S, H, D, kvdt = _common(query, key_cache, value_cache, num_kv_heads, block_tables, seq_lens,
+                            block_size, kv_cache_dtype, alibi_slopes)
+    rc = L.pav2_phase1_blocksparse(
+        _dev(exp_sums, "exp_sums"), _dev(max_logits, "max_logits"), _dev(tmp_output, "tmp_output"),
+        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        int(num_kv_heads), float(scale), _i32(block_tables, "block_tables"),
+        _i32(seq_lens, "seq_lens"), int(block_size), int(max_seq_len),
+        _dev(alibi_slopes, "alibi_slopes"), kvdt, float(k_scale), float(v_scale),
+        int(tp_rank), int(blocksparse_local_blocks), int(blocksparse_vert_stride or 0),
+        int(blocksparse_block_size), int(blocksparse_head_sliding_step),
+        S, H, D, int(key_cache.shape[0]), int(block_tables.shape[1]), int(tmp_output.shape[2]),
+        _dtype_code(query), _stream(query, stream))
+    _check(rc)
+
+
 def phase2(output, exp_sums, max_logits, tmp_output, seq_lens, stream=None) -> None:
     L = load()
     S, H, D = (int(v) for v in output.shape)
@@ -340,6 +365,18 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, kv_cache
         _dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
         _dev(slot_mapping.reshape(-1), "slot_mapping"), kvdt, float(k_scale), float(v_scale), T, KVH, D, bs, NB,
         _dtype_code(key), _stream(key, stream))
+    _check(rc)
+
+
+def read_stream(buf, sink, nontemporal=True, stream=None) -> None:
+    """Read every byte of the device tensor `buf` once (pav2_read_stream): a
+    measurement aid for achievable read bandwidth (nontemporal) and for
+    flushing the caches between timed steps (ordinary loads).  `sink` is a
+    device tensor of at least 4 bytes the kernel may write."""
+    if buf.numel() * buf.element_size() % 16:
+        raise ValueError("buf must hold a multiple of 16 bytes")
+    rc = load().pav2_read_stream(_dev(buf, "buf"), buf.numel() * buf.element_size(), 1 if nontemporal else 0,
+                                 _dev(sink, "sink"), _stream(buf, stream))
     _check(rc)
 
 

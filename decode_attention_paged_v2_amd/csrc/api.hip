@@ -424,6 +424,31 @@ int pav2_paged_attention_v2_blocksparse(void *output, float *exp_sums, float *ma
                       head_size, max_num_partitions, (int)query_dtype, st);
 }
 
+int pav2_phase1_blocksparse(float *exp_sums, float *max_logits, void *tmp_output, const void *query,
+                            const void *key_cache, const void *value_cache, int num_kv_heads, float scale,
+                            const int32_t *block_tables, const int32_t *seq_lens, int block_size, int max_seq_len,
+                            const float *alibi_slopes, pav2_dtype_t kv_cache_dtype, float k_scale, float v_scale,
+                            int tp_rank, int blocksparse_local_blocks, int blocksparse_vert_stride,
+                            int blocksparse_block_size, int blocksparse_head_sliding_step, int num_seqs,
+                            int num_heads, int head_size, int num_blocks, int max_blocks_per_seq,
+                            int max_num_partitions, pav2_dtype_t query_dtype, pav2_stream_t stream) {
+    g_err[0] = 0;
+    Shape sh{num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks,
+             max_blocks_per_seq, max_num_partitions, max_seq_len, (int)query_dtype, (int)kv_cache_dtype};
+    int rc = check_shape(sh);
+    if (rc) return rc;
+    const Sparse sp{tp_rank, blocksparse_local_blocks, blocksparse_vert_stride, blocksparse_block_size,
+                    blocksparse_head_sliding_step};
+    rc = check_sparse(sp, sh);
+    if (rc) return rc;
+    if (num_seqs == 0) return PAV2_OK;
+    rc = check_phase1_args(exp_sums, max_logits, tmp_output, query, key_cache, value_cache,
+                           block_tables, seq_lens, scale, k_scale, v_scale);
+    if (rc) return rc;
+    return run_phase1(exp_sums, max_logits, tmp_output, query, key_cache, value_cache, scale, block_tables,
+                      seq_lens, alibi_slopes, k_scale, v_scale, sh, static_cast<hipStream_t>(stream), &sp);
+}
+
 int pav2_paged_attention_v1(void *output, const void *query, const void *key_cache,
                             const void *value_cache, int num_kv_heads, float scale,
                             const int32_t *block_tables, const int32_t *seq_lens, int block_size,
@@ -647,6 +672,23 @@ int pav2_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int 
                                                    block_size, num_blocks, reinterpret_cast<long long *>(report),
                                                    static_cast<hipStream_t>(stream)),
                          "check_inputs");
+}
+
+int pav2_read_stream(const void *src, int64_t bytes, int nontemporal, uint32_t *sink, pav2_stream_t stream) {
+    g_err[0] = 0;
+    if (bytes < 0 || bytes % 16) return fail(PAV2_ERR_INVALID_ARGUMENT, "bytes (%lld) must be a multiple of 16 and >= 0",
+                                             (long long)bytes);
+    if (bytes == 0) return PAV2_OK;
+    if (!src || !sink) return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    // four workgroups per compute unit, each sweeping one contiguous slab
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+    }
+    return launch_status(pav2::launch_read_stream(src, bytes, nontemporal != 0, sink, 4 * cus,
+                                                  static_cast<hipStream_t>(stream)),
+                         "read_stream");
 }
 
 int pav2_max_num_partitions(int max_seq_len) {

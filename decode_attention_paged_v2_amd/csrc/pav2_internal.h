@@ -81,6 +81,8 @@ hipError_t launch_phase2(const Phase2Params &p, int odt, int head_size, int thre
                          int lds_bytes, hipStream_t stream);
 hipError_t launch_decode_kv(const void *src, float *dst, int64_t n, int dtype, int via,
                             hipStream_t stream);
+hipError_t launch_read_stream(const void *src, int64_t bytes, bool nontemporal, uint32_t *sink, int workgroups,
+                              hipStream_t stream);
 hipError_t launch_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
                                int max_blocks_per_seq, int block_size, int num_blocks, long long *report,
                                hipStream_t stream);

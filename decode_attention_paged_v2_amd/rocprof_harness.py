@@ -97,7 +97,11 @@ def _bench_args(config: str, mode: str, steps: int, warmup: int, entry: str = "v
             "--no-cpu-baseline"]
     if mode in ("cache_write", "prefix"):
         return args + ["--mode", mode]
-    return args + ["--flush-steps", "0"] + (["--entry", "v1"] if entry == "v1" else [])
+    # the benchmark's own flushed steps (a read sweep before each), one workload
+    args = args + ["--single"]
+    if mode == "blocksparse":
+        return args + ["--mode", "blocksparse"]
+    return args + (["--entry", "v1"] if entry == "v1" else [])
 
 
 def _tag(mode: str, config: str, entry: str) -> str:
@@ -185,7 +189,7 @@ def sq(config: str, out: str) -> dict:
         d = os.path.join(out, f"sq{i}_{config}")
         shutil.rmtree(d, ignore_errors=True)
         bench = [sys.executable, BENCH, "--config", config, "--steps", "3", "--warmup", "1",
-                 "--no-cpu-baseline", "--flush-steps", "0"]
+                 "--no-cpu-baseline", "--single"]
         cmd = ["rocprofv3", "--pmc", *counters, "-d", d, "-o", "run", "--output-format", "csv", "--"] + bench
         _run(cmd, os.path.join(out, f"sq{i}_{config}.log"), 120)
         per = {}
@@ -220,19 +224,25 @@ def algorithmic_bytes(config: str) -> dict:
 def write_summary(config: str, out: str, trace: dict, counters: dict | None, sqv: dict | None = None,
                   entry: str = "v2") -> str:
     alg = dict(algorithmic_bytes(config))
+    if entry == "blocksparse":
+        # the attended K/V only (the benchmark's pattern)
+        from . import accounting, workloads
+        import bench
+        alg = dict(accounting.blocksparse_spec_bytes(workloads.SPECS[config], bench.BLOCKSPARSE_PATTERN))
     if entry == "v1":
         # the single pass reads what phase 1 reads and writes the final rows only
         alg["phase1"] = alg["v1"]
         alg["phase1_write"] = alg["v1"] - alg["phase1_read"]
     p1 = trace["phase1"]
-    name = ("phase1_" if entry == "v2" else "v1_") + config
-    title = "Phase 1 / phase 2" if entry == "v2" else "Single-pass (V1)"
-    label = "Phase-1" if entry == "v2" else "Single-pass"
+    name = {"v2": "phase1_", "v1": "v1_", "blocksparse": "blocksparse_"}[entry] + config
+    title = {"v2": "Phase 1 / phase 2", "v1": "Single-pass (V1)", "blocksparse": "Block-sparse phase 1 / phase 2"}[entry]
+    label = {"v2": "Phase-1", "v1": "Single-pass", "blocksparse": "Block-sparse phase-1"}[entry]
     lines = [f"# {title} profile: {config}", "",
              f"Kernel sources hash: `{source_hash()}`", "",
              "Kernel trace command (from the repository root):", "",
              "    python -m decode_attention_paged_v2_amd.rocprof_harness --config "
-             f"{config}{' --entry v1' if entry == 'v1' else ''} --out gpurun_out/prof"
+             f"{config}{' --entry v1' if entry == 'v1' else ''}"
+             f"{' --mode blocksparse' if entry == 'blocksparse' else ''} --out gpurun_out/prof"
              f"{' --pmc' if counters else ''}{' --sq' if sqv else ''}", "",
              "which runs:", "", "    " + trace["command"], "",
              "| kernel | calls | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|"]
@@ -389,7 +399,7 @@ def write_prefix_summary(out: str, trace: dict, counters: dict | None = None) ->
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="long_gqa")
-    ap.add_argument("--mode", default="decode", choices=["decode", "cache_write", "prefix"])
+    ap.add_argument("--mode", default="decode", choices=["decode", "blocksparse", "cache_write", "prefix"])
     ap.add_argument("--out", default="gpurun_out/prof")
     ap.add_argument("--pmc", action="store_true", help="HBM FETCH_SIZE / WRITE_SIZE passes")
     ap.add_argument("--sq", action="store_true", help="instruction-mix / utilisation passes")
@@ -407,6 +417,8 @@ def main():
     counters = pmc(a.config, out, a.mode, a.entry) if a.pmc else None
     if a.mode == "cache_write":
         path = write_cache_summary(a.config, out, trace, counters)
+    elif a.mode == "blocksparse":
+        path = write_summary(a.config, out, trace, counters, None, "blocksparse")
     else:
         sqv = sq(a.config, out) if a.sq else None
         path = write_summary(a.config, out, trace, counters, sqv, a.entry)

@@ -237,6 +237,25 @@ int pav2_phase1(
     pav2_stream_t stream);
 
 /*
+ * Block-sparse phase 1 alone (same arguments as
+ * pav2_paged_attention_v2_blocksparse without `output`).
+ */
+int pav2_phase1_blocksparse(
+    float *exp_sums, float *max_logits, void *tmp_output,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_kv_heads, float scale,
+    const int32_t *block_tables, const int32_t *seq_lens,
+    int block_size, int max_seq_len,
+    const float *alibi_slopes,
+    pav2_dtype_t kv_cache_dtype, float k_scale, float v_scale,
+    int tp_rank, int blocksparse_local_blocks, int blocksparse_vert_stride,
+    int blocksparse_block_size, int blocksparse_head_sliding_step,
+    int num_seqs, int num_heads, int head_size, int num_blocks,
+    int max_blocks_per_seq, int max_num_partitions,
+    pav2_dtype_t query_dtype,
+    pav2_stream_t stream);
+
+/*
  * Phase 2 alone, the log-sum-exp combine: reads exp_sums, max_logits and
  * tmp_output for partitions p < min(ceil(seq_lens[s]/512), max_num_partitions)
  * and writes output (dtype `out_dtype`, which is also tmp_output's dtype).
@@ -367,6 +386,19 @@ int pav2_reshape_and_cache(
 int pav2_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
                       int max_blocks_per_seq, int block_size, int num_blocks, int64_t *report,
                       pav2_stream_t stream);
+
+/*
+ * Measurement aid, not part of the attention path: read `bytes` (a multiple
+ * of 16) of device memory at `src` once with 16-byte vector loads, four
+ * workgroups per compute unit each sweeping one contiguous slab.  With
+ * nontemporal != 0 the loads carry the streaming hint phase 1 uses for K/V
+ * (the chip's achievable read bandwidth for that access); with 0 they are
+ * ordinary loads that allocate in L2 and the Infinity Cache, evicting their
+ * contents without dirtying them (a cache flush between timed steps).
+ * `sink` is one uint32 of caller device memory that the kernel may write.
+ * Asynchronous on `stream`; allocates nothing.
+ */
+int pav2_read_stream(const void *src, int64_t bytes, int nontemporal, uint32_t *sink, pav2_stream_t stream);
 
 /* ceil(max_seq_len / 512): the partition count a sequence of that length needs. */
 int pav2_max_num_partitions(int max_seq_len);

@@ -42,3 +42,28 @@ def test_long_context_workload_bytes():
     assert b["phase1"] == b["phase1_read"] + b["phase1_write"]
     # the single pass reads the same and writes only the output rows
     assert b["v1"] == b["phase1_read"] + 4 * 24 * 256 * 2
+
+
+def test_blocksparse_attended_tokens_hand_counts():
+    # the golden case of tests/golden/blocksparse_positions.json: L = 100, B = 16,
+    # local 2, stride 3, step 1: heads 0, 1, 2 attend 52, 52, 36 tokens; together
+    # every block 0..6 (100 tokens)
+    pat = (0, 2, 3, 16, 1)
+    assert [accounting.blocksparse_attended_tokens(100, [h], 3, pat) for h in range(3)] == [52, 52, 36]
+    assert accounting.blocksparse_attended_tokens(100, [0, 1, 2], 3, pat) == 100
+    # dense when the stride is <= 1; nothing for an empty sequence
+    assert accounting.blocksparse_attended_tokens(100, [0], 3, (0, 0, 1, 16, 0)) == 100
+    assert accounting.blocksparse_attended_tokens(0, [0], 3, pat) == 0
+
+
+def test_blocksparse_bytes_of_the_benchmark_pattern():
+    # long-context workload, 64-token blocks, 16-block window, every 8th block, same
+    # stripes for all heads: per sequence 100000 tokens = blocks 0..1562 (the last
+    # one 32 tokens); window 1547..1562 = 15 * 64 + 32 tokens; stripes 0, 8, ..,
+    # 1544 = 194 blocks outside the window (1552, 1560 lie inside it)
+    L, B = 100000, 64
+    window = 15 * 64 + 32
+    stripes = len([k for k in range(0, 1547, 8)]) * 64
+    assert accounting.blocksparse_attended_tokens(L, list(range(6)), 24, (0, 16, 8, B, 0)) == window + stripes
+    kv = accounting.blocksparse_kv_bytes([L] * 4, 24, 4, 256, 2, (0, 16, 8, B, 0))
+    assert kv == 4 * 4 * (window + stripes) * 2 * 256 * 2
