@@ -19,8 +19,8 @@ LIB = os.path.join(HERE, "libpav2.so")
 # phase 1's kernel variants are split by (query dtype, cache dtype) pair so they compile in parallel
 PHASE1_PAIRS = ["f32_f32", "f16_f16", "bf16_bf16", "f32_fp8", "f16_fp8", "bf16_fp8"]
 SOURCES = (["api.hip", "phase1.hip"] + [f"phase1_{p}.hip" for p in PHASE1_PAIRS] +
-           [f"phase1_sparse_{p}.hip" for p in PHASE1_PAIRS] + ["phase2.hip", "check.hip", "cache.hip", "stream.hip"])
-HEADERS = [os.path.join(CSRC, h) for h in ("pav2_internal.h", "phase1_kernel.h", "cache.h")] + \
+           [f"phase1_sparse_{p}.hip" for p in PHASE1_PAIRS] + ["phase2.hip", "check.hip", "cache.hip", "stream.hip", "prefix.hip"])
+HEADERS = [os.path.join(CSRC, h) for h in ("pav2_internal.h", "phase1_kernel.h", "cache.h", "prefix.h")] + \
     [os.path.join(ROOT, "include", "pav2.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -11,6 +11,7 @@
 #include "../../include/pav2.h"
 #include "pav2_internal.h"
 #include "cache.h"
+#include "prefix.h"
 
 namespace {
 
@@ -564,13 +565,38 @@ int pav2_paged_prefix_attention(void *output, const void *query, const void *key
     int rc = check_shape(sh);
     if (rc) return rc;
     const int gqa = num_heads / num_kv_heads;
-    const int64_t row_blocks = ((int64_t)max_query_len * gqa + pav2::kPrefixRows - 1) / pav2::kPrefixRows;
+    const bool mfma = pav2::prefix_mfma_supported((int)dtype, head_size, ilog2_exact(block_size), scale);
+    const int rows_per_wg = mfma ? pav2::kPrefixMfmaRows : pav2::kPrefixRows;
+    const int64_t row_blocks = ((int64_t)max_query_len * gqa + rows_per_wg - 1) / rows_per_wg;
     const int64_t work = (int64_t)num_seqs * num_kv_heads * row_blocks;
     if (work > ((int64_t)1 << 31) - 1 || row_blocks > ((int64_t)1 << 30))
         return fail(PAV2_ERR_UNSUPPORTED, "num_seqs * num_kv_heads * row blocks = %lld is too large", (long long)work);
     if (work == 0) return PAV2_OK;
     if (!output || !query || !key_cache || !value_cache || !block_tables || !query_start_loc || !context_lens)
         return fail(PAV2_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (mfma) {
+        pav2::PrefixParams q;
+        q.out = output;
+        q.query = query;
+        q.key_cache = static_cast<const uint8_t *>(key_cache);
+        q.value_cache = static_cast<const uint8_t *>(value_cache);
+        q.block_tables = block_tables;
+        q.query_start_loc = query_start_loc;
+        q.context_lens = context_lens;
+        q.num_seqs = num_seqs;
+        q.num_heads = num_heads;
+        q.num_kv_heads = num_kv_heads;
+        q.gqa = gqa;
+        q.row_blocks = (int)row_blocks;
+        q.bs_log2 = ilog2_exact(block_size);
+        q.max_blocks_per_seq = max_blocks_per_seq;
+        q.num_work = (int)work;
+        q.head_stride = (int64_t)head_size * block_size * elem_bytes(dtype);
+        q.blk_stride = q.head_stride * num_kv_heads;
+        q.scale_log2 = scale * 1.4426950408889634f;
+        return launch_status(pav2::launch_prefix(q, (int)dtype, head_size, static_cast<hipStream_t>(stream)),
+                             "prefix attention");
+    }
     pav2::Phase1Params p;
     p.tmp_out = output;
     p.exp_sums = nullptr;

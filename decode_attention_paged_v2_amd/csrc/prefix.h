@@ -1,0 +1,33 @@
+// Paged prefix attention on MFMA tiles: launch parameters shared by the C ABI
+// and the kernel (csrc/prefix.hip).
+#pragma once
+
+#include "pav2_internal.h"
+
+namespace pav2 {
+
+struct PrefixParams {
+    void *out;                       // [T, H, D] dtype
+    const void *query;               // [T, H, D]
+    const uint8_t *key_cache;        // [NB, KVH, D/8, BS, 8]
+    const uint8_t *value_cache;      // [NB, KVH, D, BS]
+    const int32_t *block_tables;     // [S, MBPS]
+    const int32_t *query_start_loc;  // [S + 1]
+    const int32_t *context_lens;     // [S]
+    int num_seqs, num_heads, num_kv_heads, gqa;
+    int row_blocks;                  // ceil(max_query_len * gqa / 128)
+    int bs_log2, max_blocks_per_seq;
+    int num_work;                    // num_seqs * num_kv_heads * row_blocks
+    int64_t blk_stride, head_stride;
+    float scale_log2;                // scale * log2(e)
+};
+
+constexpr int kPrefixMfmaRows = 128;   // query rows per workgroup
+
+// Whether the MFMA-tile kernel serves this case (16-bit caches, head size a
+// multiple of 32, blocks of at least 8 tokens, a positive scale); others take
+// phase 1's prefix schedule.
+bool prefix_mfma_supported(int dtype, int head_size, int bs_log2, float scale);
+hipError_t launch_prefix(const PrefixParams &p, int dtype, int head_size, hipStream_t stream);
+
+}  // namespace pav2

@@ -43,7 +43,8 @@ BENCH = os.path.join(ROOT, "bench.py")
 _PLAN = [os.path.join(HERE, "csrc", "api.hip"), os.path.join(ROOT, "include", "pav2.h")]
 KERNEL_SOURCES = {
     "decode": sorted(glob.glob(os.path.join(HERE, "csrc", "phase1*"))) +
-              [os.path.join(HERE, "csrc", f) for f in ("phase2.hip", "pav2_internal.h")] + _PLAN,
+              [os.path.join(HERE, "csrc", f) for f in ("phase2.hip", "pav2_internal.h", "prefix.hip", "prefix.h")]
+              + _PLAN,
     "cache_write": [os.path.join(HERE, "csrc", f) for f in ("cache.hip", "cache.h", "pav2_internal.h")] + _PLAN,
 }
 
