@@ -594,6 +594,7 @@ int pav2_paged_prefix_attention(void *output, const void *query, const void *key
         q.head_stride = (int64_t)head_size * block_size * elem_bytes(dtype);
         q.blk_stride = q.head_stride * num_kv_heads;
         q.scale_log2 = scale * 1.4426950408889634f;
+        q.offsets32 = (int64_t)num_blocks * q.blk_stride <= ((int64_t)1 << 32);
         return launch_status(pav2::launch_prefix(q, (int)dtype, head_size, static_cast<hipStream_t>(stream)),
                              "prefix attention");
     }

@@ -20,6 +20,10 @@ struct PrefixParams {
     int num_work;                    // num_seqs * num_kv_heads * row_blocks
     int64_t blk_stride, head_stride;
     float scale_log2;                // scale * log2(e)
+    // every byte of a kv head's cache slab lies within 4 GiB of the slab's
+    // first block (num_blocks * blk_stride <= 2^32): the tiles are then copied
+    // with buffer (32-bit offset) loads into LDS, else with global ones
+    bool offsets32;
 };
 
 constexpr int kPrefixMfmaRows = 128;   // query rows per workgroup

@@ -47,7 +47,6 @@ namespace {
 constexpr int kRows = 128;     // query rows per workgroup (4 wavefronts x 32)
 constexpr int kKeys = 64;      // keys per tile
 constexpr float kLazy = 8.0f;  // log2 headroom before the running offset moves
-constexpr int kPre = 4;        // LDS fragment reads issued ahead of the MFMAs
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
@@ -58,6 +57,15 @@ template <int N>
 struct IC {   // a compile-time int argument for generic lambdas
     static constexpr int value = N;
 };
+
+// f(IC<I>{}), f(IC<I + 1>{}), ..., f(IC<N - 1>{})
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(IC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -94,7 +102,13 @@ __device__ __forceinline__ float unpack16(uint32_t w) {
 // SPLIT: the weights enter P V as two 16-bit parts (hi + the rounding
 // residual, ~16 significant bits); bfloat16's 8-bit significand alone moves
 // the output of rows with few visible keys by more than the tolerance.
-template <int DT, int D, bool SPLIT = (DT == BF16)>
+// BUF: the tiles are copied with buffer loads (32-bit offsets from the kv
+// head's slab, which must span at most 4 GiB).  The compiler counts a global
+// load into LDS as a possible LDS access of its own and so waits for every
+// outstanding LDS read wherever one is pending; with buffer loads its waits
+// for the fragment reads stay partial (the hardware counts neither form
+// against the LDS counter).
+template <int DT, int D, bool BUF, bool SPLIT = (DT == BF16)>
 __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
     static_assert(D % 32 == 0 && D <= 256, "head size: whole 32-row output tiles");
     constexpr int NC = D / 8;                 // 16-byte K chunks per token
@@ -104,6 +118,8 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
     constexpr int VI = (D + 63) / 64;         // V copies (64 rows each) per 8-key group
     constexpr int KPW = NC / 4;               // K copies per wavefront per tile
     constexpr int VPW = 2 * VI;               // V copies per wavefront per tile
+    constexpr int SW = NS % 2 == 0 ? 2 : 1;   // contraction steps per pipeline slot
+    constexpr int NSLOT = NS / SW;            // slots per 32-key step
     static_assert(NC % 4 == 0, "K copies split over 4 wavefronts");
     __shared__ __align__(16) uint8_t k0[TILE], k1[TILE], v0[TILE], v1[TILE];
 
@@ -161,37 +177,53 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
     const uint8_t *kc = P.key_cache + (int64_t)g * P.head_stride;
     const uint8_t *vc = P.value_cache + (int64_t)g * P.head_stride;
     const int64_t blk_stride = P.blk_stride;
+    // buffer resources over the kv head's slabs (raw, byte offsets, 32-bit
+    // data format word as gfx9 wants; no range limit below 4 GiB)
+    __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(kc), 0, -1, 0x00020000);
+    __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(vc), 0, -1, 0x00020000);
 
-    // block of key t0 + lane of a tile (lanes past the limit: 0, never used)
-    auto key_block = [&](int t) -> int {
-        const int key = t * kKeys + lane;
-        return key < Lmax ? bt[key >> bs_log2] : 0;
+    // block of key t * kKeys + lane, clamped to the block's last key: every
+    // K slot of a copied tile holds a real (finite) key; the surplus ones meet
+    // the causal mask
+    auto key_block = [&](int t) -> int { return bt[min(t * kKeys + lane, Lmax - 1) >> bs_log2]; };
+    // one copy instruction of a tile: K chunk row wv * KPW + k (64 keys x 16
+    // bytes), or V instruction k of this wavefront (64 head-dim rows of one
+    // 8-key group)
+    auto copy_k_one = [&](int k, int t, int blk, uint8_t *kd) __attribute__((always_inline)) {
+        const int key = min(t * kKeys + lane, Lmax - 1);
+        const int c = wv * KPW + k;
+        const int64_t off = (int64_t)blk * blk_stride + (((int64_t)c << bs_log2) + (key & bs_mask)) * 16;
+        if constexpr (BUF)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr)(kd + c * kKeys * 16), 16, (uint32_t)off, 0, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(kc + off, (lds_ptr)(kd + c * kKeys * 16), 16, 0, 0);
     };
-    // copy tile t into (kd, vd): this wavefront's K chunks and V rows
-    auto copy_tile = [&](int t, int blk, uint8_t *kd, uint8_t *vd) {
+    // V: groups of 8 keys (one block each, as block sizes are >= 8); a group
+    // past the block's limit takes the last group that holds a key below it,
+    // and the last tile's keys past the limit are zeroed before use
+    auto copy_v_one = [&](int k, int t, int blk, uint8_t *vd) __attribute__((always_inline)) {
         const int t0 = t * kKeys;
-        const int key = t0 + lane;
-#pragma unroll
-        for (int k = 0; k < KPW; ++k) {
-            const int c = wv * KPW + k;
-            if (key < Lmax) {
-                const uint8_t *src = kc + (int64_t)blk * blk_stride + (((int64_t)c << bs_log2) + (key & bs_mask)) * 16;
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(kd + c * kKeys * 16), 16, 0, 0);
-            }
+        const int ki = wv * VPW + k;
+        const int kg = ki / VI, d0 = (ki % VI) * 64;
+        const int d = d0 + lane;
+        const int kgs = min(kg, (Lmax - 1 - t0) >> 3);   // source group (uniform)
+        const int gb = __builtin_amdgcn_readlane(blk, 8 * kgs);
+        if (D % 64 == 0 || d < D) {   // (head sizes of 64 k + 32: the last copy's upper half-wave idles)
+            const int64_t off = (int64_t)gb * blk_stride + (((int64_t)d << bs_log2) + ((t0 + 8 * kgs) & bs_mask)) * 2;
+            if constexpr (BUF)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr)(vd + (kg * D + d0) * 16), 16, (uint32_t)off, 0, 0,
+                                                         0);
+            else
+                __builtin_amdgcn_global_load_lds(vc + off, (lds_ptr)(vd + (kg * D + d0) * 16), 16, 0, 0);
         }
+    };
+    auto copy_k = [&](int t, int blk, uint8_t *kd) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < VPW; ++k) {
-            const int ki = wv * VPW + k;
-            const int kg = ki / VI, d0 = (ki % VI) * 64;
-            const int d = d0 + lane;
-            // the group's 8 keys share one block (block sizes >= 8 here)
-            const int gb = __builtin_amdgcn_readlane(blk, 8 * kg);
-            if (8 * kg < Lmax - t0 && d < D) {
-                const uint8_t *src = vc + (int64_t)gb * blk_stride +
-                                     (((int64_t)d << bs_log2) + ((t0 + 8 * kg) & bs_mask)) * 2;
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(vd + (kg * D + d0) * 16), 16, 0, 0);
-            }
-        }
+        for (int k = 0; k < KPW; ++k) copy_k_one(k, t, blk, kd);
+    };
+    auto copy_v = [&](int t, int blk, uint8_t *vd) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < VPW; ++k) copy_v_one(k, t, blk, vd);
     };
 
     f32x16 o[NDT];
@@ -199,124 +231,225 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
-    float lsum = 0.0f;          // this half-wave's share of the row's rounded-weight sum
+    float lsum = 0.0f;          // this half-wave's share of the row's weight sum
     float m_used = -INFINITY;   // running offset (log2 units) of the weights
     const float sl2 = P.scale_log2;
+    f32x16 s_cur;               // raw scores S^T of the half being turned into weights
+    u32x4 p_prev[2][2];         // [16-key step][hi, lo]: weights of the half whose P.V is pending
+    const int koff = (half * kKeys + lrow) * 16;   // A of S^T: key 32 nt + lrow, chunk 2 st + half
+    const int voff = (half * D + lrow) * 16;       // A of O^T: group 2 ks + half, row 32 dt + lrow
+    // this lane's fragment base in each buffer, held in a register the
+    // compiler does not fold back into constants, so every fragment read adds
+    // its offset (< 64 KiB) in the instruction (the buffers span 4 x D x 128
+    // bytes); the pointer stays derived from its buffer for alias analysis
+    auto lane_base = [&](uint8_t *buf, int off) -> const uint8_t * {
+        const uint32_t a = (uint32_t)(uintptr_t)(lds_ptr)buf;
+        uint32_t x = a + (uint32_t)off;
+        asm volatile("" : "+v"(x));
+        return buf + (x - a);
+    };
+    const uint8_t *const kl0 = lane_base(k0, koff), *const kl1 = lane_base(k1, koff);
+    const uint8_t *const vl0 = lane_base(v0, voff), *const vl1 = lane_base(v1, voff);
 
-    // one tile, as two halves of 32 keys: S^T, mask, max, weights, O^T
-    auto compute = [&](int t, const uint8_t *kb, const uint8_t *vb) {
-        const int t0 = t * kKeys;
-        const uint8_t *kl = kb + (half * kKeys + lrow) * 16;   // A of S^T: key 32 nt + lrow, chunk 2 st + half
-        const uint8_t *vl = vb + (half * D + lrow) * 16;       // A of O^T: group 2 ks + half, row 32 dt + lrow
-        auto half_tile = [&](auto ntc) {
-            constexpr int nt = decltype(ntc)::value;
-            f32x16 acc;
+    // the weights of one half from its scores, offset by -nmu (log2 units):
+    // element i of s is key 8 (i / 4) + 4 half + i % 4 of the half; returns
+    // this half-wave's sum of the weights as they enter the MFMAs
+    auto weights = [&](const f32x16 &s, float nmu, u32x4 (&p)[2][2]) __attribute__((always_inline)) -> float {
+        float part = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+        for (int kh = 0; kh < 2; ++kh) {   // the half's two steps of 16 keys (k-groups ke, ko)
+            const int ke = 2 * kh, ko = ke + 1;
+            float pv[8];
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(kl + (2 * st * kKeys + 32 * nt) * 16);
-                acc = mfma32<DT>(a, qf[st], acc);
+            for (int i = 0; i < 4; ++i) {
+                pv[i] = __builtin_amdgcn_exp2f(fmaf(s[4 * ke + i], sl2, nmu));
+                pv[4 + i] = __builtin_amdgcn_exp2f(fmaf(s[4 * ko + i], sl2, nmu));
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, kPre, 2 * nt);   // kPre LDS reads ahead
+            uint32_t w[4] = {pack16<DT>(pv[0], pv[1]), pack16<DT>(pv[2], pv[3]), pack16<DT>(pv[4], pv[5]),
+                             pack16<DT>(pv[6], pv[7])};
+            uint32_t r[4] = {0u, 0u, 0u, 0u};
+            if constexpr (SPLIT) {   // the rounding residual as a second 16-bit part
 #pragma unroll
-            for (int f = 0; f < NS - kPre; ++f) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2 * nt);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 2 * nt);
+                for (int k = 0; k < 4; ++k)
+                    r[k] = pack16<DT>(pv[2 * k] - unpack16<DT, 0>(w[k]), pv[2 * k + 1] - unpack16<DT, 1>(w[k]));
+                // hi + lo equals the float32 weight to ~2^-17: sum the weights
+                part += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+            } else {   // one 16-bit part: sum the weights as rounded
+#pragma unroll
+                for (int k = 0; k < 4; ++k) part += unpack16<DT, 0>(w[k]) + unpack16<DT, 1>(w[k]);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, kPre, 2 * nt);
+            // half 0 held keys 0-3 and 8-11 of the step, half 1 keys 4-7 and
+            // 12-15: one swap per register pair gives half h keys 8 h .. 8 h + 7
+            auto regroup = [](uint32_t (&x)[4]) {
+                const auto a0 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+                const auto a1 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+                x[0] = a0[0];
+                x[2] = a0[1];
+                x[1] = a1[0];
+                x[3] = a1[1];
+            };
+            regroup(w);
+            if constexpr (SPLIT) regroup(r);
+            p[kh][0] = u32x4{w[0], w[1], w[2], w[3]};
+            p[kh][1] = u32x4{r[0], r[1], r[2], r[3]};
+        }
+        return part;
+    };
 
-            // element i: key t0 + 32 nt + 8 (i / 4) + 4 half + i % 4; the
-            // scale (> 0) is applied with the offset, in one FMA per weight
-            if (t0 + 32 * nt + 32 > lmin) {   // the half reaches some row's causal limit (uniform)
-                const int rel = lim - t0 - 32 * nt - 4 * half;
+    // One step of the pipeline over 32-key halves, flags F: 1 = P.V of the
+    // pending half (weights p_prev, V fragments at vl, half vnt of its tile);
+    // 2 = S^T of the next half (K fragments at kl, half knt); 4 = weights of
+    // half h from s_cur.  The step runs in NS slots; slot i issues the LDS
+    // reads of slot i + kAhead, the MFMAs of slot i (S^T contraction step i,
+    // V fragment i) and a share of the weights' VALU work, fenced so that the
+    // reads keep their distance and the VALU work fills the MFMAs' shadow.
+    // The rare rescale of the accumulators follows the slots.
+    auto step = [&](auto flags, const uint8_t *vl, int vnt, const uint8_t *kl, int knt, int h, auto &&dma)
+                    __attribute__((always_inline)) {
+        constexpr int F = decltype(flags)::value;
+        constexpr bool DO_PV = F & 1, DO_QK = F & 2, DO_SM = F & 4;
+        if constexpr (DO_SM) {
+            if (32 * h + 32 > lmin) {   // the half reaches some row's causal limit (uniform)
+                const int rel = lim - 32 * h - 4 * half;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[i] = (8 * (i / 4) + (i % 4)) < rel ? acc[i] : -INFINITY;
+                for (int i = 0; i < 16; ++i) s_cur[i] = (8 * (i / 4) + (i % 4)) < rel ? s_cur[i] : -INFINITY;
             }
-            float mx = acc[0];
+        }
+        auto kfrag = [&](int i) { return *reinterpret_cast<const u32x4 *>(kl + (2 * i * kKeys + 32 * knt) * 16); };
+        auto vfrag = [&](int i) {
+            return *reinterpret_cast<const u32x4 *>(vl + (2 * (2 * vnt + i / NDT) * D + 32 * (i % NDT)) * 16);
+        };
+        f32x16 acc;
 #pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;   // the other half-wave holds the row's other keys
-            if (mx > m_used + kLazy) {   // move the offset; rescale what was accumulated
-                const float alpha = __builtin_amdgcn_exp2f(m_used - mx);   // 0 on the first visible keys
-                m_used = mx;
+        for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+        // fragments of slot j + 1 are read while slot j multiplies: slots of
+        // SW contraction steps (and SW V fragments), so each wait for LDS has
+        // a slot of MFMAs and VALU work behind it
+        u32x4 kr[2][SW], vr[2][SW];   // [slot parity][step in slot]
+        static_for<0, SW>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (DO_QK) kr[0][j] = kfrag(j);
+            if constexpr (DO_PV) vr[0][j] = vfrag(j);
+        });
+        // weights of the current half under the current offset: pieces 0-7
+        // each turn 2 scores into a packed pair (and its residual), piece 8
+        // takes the row maximum, piece 9 regroups the pairs into B operands
+        const float nmu = m_used == -INFINITY ? 0.0f : -m_used;
+        uint32_t w[2][4], r[2][4];
+        float part = 0.0f, mxs = -INFINITY;
+        u32x4 p_cur[2][2];
+        auto piece = [&](auto pc) {
+            constexpr int pi = decltype(pc)::value;
+            if constexpr (pi < 8) {
+                constexpr int kh = pi / 4, k = pi % 4;
+                constexpr int i0 = k < 2 ? 4 * (2 * kh) + 2 * k : 4 * (2 * kh + 1) + 2 * (k - 2);
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(s_cur[i0], sl2, nmu));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(s_cur[i0 + 1], sl2, nmu));
+                w[kh][k] = pack16<DT>(e0, e1);
+                if constexpr (SPLIT) {   // the rounding residual as a second 16-bit part
+                    r[kh][k] = pack16<DT>(e0 - unpack16<DT, 0>(w[kh][k]), e1 - unpack16<DT, 1>(w[kh][k]));
+                    part += e0 + e1;   // hi + lo equals the float32 weight to ~2^-17
+                } else {
+                    r[kh][k] = 0u;
+                    part += unpack16<DT, 0>(w[kh][k]) + unpack16<DT, 1>(w[kh][k]);   // as rounded
+                }
+            } else if constexpr (pi == 8) {
+                float mx = s_cur[0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s_cur[i]);
+                const auto sw =
+                    __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mxs = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;   // both half-waves' keys
+            } else {
+                // half 0 held keys 0-3 and 8-11 of a 16-key step, half 1 keys
+                // 4-7 and 12-15: one swap per register pair gives half h keys
+                // 8 h .. 8 h + 7
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const auto a0 = __builtin_amdgcn_permlane32_swap(w[kh][0], w[kh][2], false, false);
+                    const auto a1 = __builtin_amdgcn_permlane32_swap(w[kh][1], w[kh][3], false, false);
+                    p_cur[kh][0] = u32x4{a0[0], a1[0], a0[1], a1[1]};
+                    if constexpr (SPLIT) {
+                        const auto b0 = __builtin_amdgcn_permlane32_swap(r[kh][0], r[kh][2], false, false);
+                        const auto b1 = __builtin_amdgcn_permlane32_swap(r[kh][1], r[kh][3], false, false);
+                        p_cur[kh][1] = u32x4{b0[0], b1[0], b0[1], b1[1]};
+                    } else {
+                        p_cur[kh][1] = u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+            }
+        };
+        static_for<0, NSLOT>([&](auto jc) {
+            constexpr int j = decltype(jc)::value, cur = j & 1;
+            if constexpr (j + 1 < NSLOT) {
+                static_for<0, SW>([&](auto ec) {
+                    constexpr int e = decltype(ec)::value;
+                    if constexpr (DO_QK) kr[cur ^ 1][e] = kfrag(SW * (j + 1) + e);
+                    if constexpr (DO_PV) vr[cur ^ 1][e] = vfrag(SW * (j + 1) + e);
+                });
+            }
+            static_for<0, SW>([&](auto ec) {
+                constexpr int e = decltype(ec)::value, i = SW * j + e;
+                if constexpr (DO_QK) acc = mfma32<DT>(kr[cur][e], qf[i], acc);
+                if constexpr (DO_PV) {
+                    constexpr int kh = i / NDT, dt = i % NDT;
+                    o[dt] = mfma32<DT>(vr[cur][e], p_prev[kh][0], o[dt]);
+                    if constexpr (SPLIT) o[dt] = mfma32<DT>(vr[cur][e], p_prev[kh][1], o[dt]);
+                }
+            });
+            if constexpr (DO_SM) {
+                static_for<0, 10>([&](auto pc) {
+                    if constexpr (decltype(pc)::value * NSLOT / 10 == j) piece(pc);
+                });
+            }
+            dma(jc);   // this slot's share of the next tiles' copies
+            // order inside the slot: the next slot's reads, then MFMAs with
+            // VALU work between them (copies go where they fall)
+            constexpr int NRD = j + 1 < NSLOT ? SW * ((DO_QK ? 1 : 0) + (DO_PV ? 1 : 0)) : 0;
+            constexpr int NMF = SW * ((DO_QK ? 1 : 0) + (DO_PV ? (SPLIT ? 2 : 1) : 0));
+            if constexpr (NRD > 0) __builtin_amdgcn_sched_group_barrier(0x100, NRD, j);
+            static_for<0, NMF>([&](auto) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, j);
+                if constexpr (DO_SM) __builtin_amdgcn_sched_group_barrier(0x002, 4, j);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (DO_SM) {
+            // some row's offset moves (rare; a wave-uniform jump, so the common
+            // case runs none of it): those rows rescale what they accumulated
+            // and redo their weights, the others keep theirs (alpha = 1)
+            const bool move = mxs > m_used + kLazy;
+            if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
+                const float m_new = move ? mxs : m_used;
+                const float alpha = move ? __builtin_amdgcn_exp2f(m_used - mxs) : 1.0f;   // 0 on the first keys
+                m_used = m_new;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
                 lsum *= alpha;
+                part = weights(s_cur, m_new == -INFINITY ? 0.0f : -m_new, p_cur);
             }
-            const float mu = m_used == -INFINITY ? 0.0f : m_used;
-            const float nmu = -mu;
-
+            lsum += part;
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {   // the half's two steps of 16 keys (k-groups ke, ko)
-                const int ks = 2 * nt + kh, ke = 2 * kh, ko = ke + 1;
-                float pv[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pv[i] = __builtin_amdgcn_exp2f(fmaf(acc[4 * ke + i], sl2, nmu));
-                    pv[4 + i] = __builtin_amdgcn_exp2f(fmaf(acc[4 * ko + i], sl2, nmu));
-                }
-                uint32_t w[4] = {pack16<DT>(pv[0], pv[1]), pack16<DT>(pv[2], pv[3]), pack16<DT>(pv[4], pv[5]),
-                                 pack16<DT>(pv[6], pv[7])};
-                uint32_t r[4] = {0u, 0u, 0u, 0u};
-                if constexpr (SPLIT) {   // the rounding residual as a second 16-bit part
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        r[k] = pack16<DT>(pv[2 * k] - unpack16<DT, 0>(w[k]), pv[2 * k + 1] - unpack16<DT, 1>(w[k]));
-                }
-                // sum of the weights as they enter the MFMAs: one 16-bit part
-                // each -- or hi + lo, equal to the float32 weight to ~2^-17
-                if constexpr (SPLIT) {
-                    lsum += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) lsum += unpack16<DT, 0>(w[k]) + unpack16<DT, 1>(w[k]);
-                }
-                // half 0 held keys 0-3 and 8-11 of the step, half 1 keys 4-7 and
-                // 12-15: one swap per register pair gives half h keys 8 h .. 8 h + 7
-                auto regroup = [](uint32_t (&x)[4]) {
-                    const auto a0 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
-                    const auto a1 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
-                    x[0] = a0[0];
-                    x[2] = a0[1];
-                    x[1] = a1[0];
-                    x[3] = a1[1];
-                };
-                regroup(w);
-                if constexpr (SPLIT) regroup(r);
-                const u32x4 pb = {w[0], w[1], w[2], w[3]};
-                const u32x4 pl = {r[0], r[1], r[2], r[3]};
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(vl + (2 * ks * D + 32 * dt) * 16);
-                    o[dt] = mfma32<DT>(a, pb, o[dt]);
-                    if constexpr (SPLIT) o[dt] = mfma32<DT>(a, pl, o[dt]);
-                }
+            for (int kh = 0; kh < 2; ++kh) {
+                p_prev[kh][0] = p_cur[kh][0];
+                p_prev[kh][1] = p_cur[kh][1];
             }
-            constexpr int MPF = SPLIT ? 2 : 1;   // MFMAs per V fragment
-            constexpr int VPRE = kPre < 2 * NDT ? kPre : 2 * NDT;
-            __builtin_amdgcn_sched_group_barrier(0x100, VPRE, 2 * nt + 1);
-#pragma unroll
-            for (int f = 0; f < 2 * NDT - VPRE; ++f) {
-                __builtin_amdgcn_sched_group_barrier(0x008, MPF, 2 * nt + 1);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 2 * nt + 1);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, MPF * VPRE, 2 * nt + 1);
-        };
-        half_tile(IC<0>{});
-        half_tile(IC<1>{});
+        }
+        if constexpr (DO_QK) s_cur = acc;
     };
 
-    // the last tile's partial 8-key group: V of keys past the block's limit
-    // (other sequences' data or unwritten slots) is zeroed in LDS before use,
-    // as it meets zero weights and must not be NaN
-    auto zero_tail = [&](int t, uint8_t *vb) {
-        const int nv = Lmax - t * kKeys;   // valid keys of the tile
-        if (nv >= kKeys || (nv & 7) == 0) return;
-        const int kg = nv >> 3, keep = nv & 7;
-        for (int d = tid; d < D; d += 256) {
+    // the last tile's V past the block's limit (other sequences' data,
+    // unwritten slots or copies of a group that holds them) is zeroed in LDS
+    // before use, as it meets zero weights and must not be NaN
+    auto zero_tail = [&](int t, uint8_t *vb) __attribute__((always_inline)) {
+        const int nv = Lmax - t * kKeys;   // valid keys of the tile (1 .. 64)
+        if (nv >= kKeys) return;
+        const int g0 = nv >> 3;            // first group holding a key past the limit
+        for (int i = tid; i < (8 - g0) * D; i += 256) {
+            const int kg = g0 + i / D, d = i % D;
+            const int keep = nv - 8 * kg;  // keys of the group below the limit (<= 7, maybe <= 0)
             u32x4 *vp = reinterpret_cast<u32x4 *>(vb + (kg * D + d) * 16);
             u32x4 v = *vp;
 #pragma unroll
@@ -328,33 +461,72 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
         }
     };
 
-    // pipeline: copy t + 1 while computing t; the barrier at the top of each
-    // step finds every wavefront's copies of that tile landed and the other
-    // buffer free
-    int blk = key_block(0);
-    __syncthreads();   // the zeroed tiles are in place before any copy lands
-    copy_tile(0, blk, k0, v0);
-    blk = ntiles > 1 ? key_block(1) : 0;
-    for (int t = 0; t < ntiles; t += 2) {
-        __syncthreads();
-        if (t + 1 == ntiles) {   // last tile (uniform)
-            zero_tail(t, v0);
-            __syncthreads();
-        }
-        if (t + 1 < ntiles) copy_tile(t + 1, blk, k1, v1);
-        blk = t + 2 < ntiles ? key_block(t + 2) : 0;
-        compute(t, k0, v0);
-        if (t + 1 >= ntiles) break;
-        __syncthreads();
-        if (t + 2 == ntiles) {
-            zero_tail(t + 1, v1);
-            __syncthreads();
-        }
-        if (t + 2 < ntiles) copy_tile(t + 2, blk, k0, v0);
-        blk = t + 3 < ntiles ? key_block(t + 3) : 0;
-        compute(t + 1, k1, v1);
+    // Pipeline over tiles.  Iteration T multiplies P.V of tile T's halves and
+    // S^T of tile T + 1's, so it reads V(T) and K(T + 1) while the copies of
+    // V(T + 1) and K(T + 2) land in the other buffers; the barrier that opens
+    // it finds its tiles landed and those buffers free.  K runs one tile
+    // ahead of V.  Iterations come in pairs (static buffer choice, no exit
+    // between them), then the last tile's P.V.
+    const int N = ntiles;
+    int blk_v = key_block(0);   // block ids of the tile whose V is copied next
+    __syncthreads();            // the zeroed tiles are in place before any copy lands
+    copy_k(0, blk_v, k0);
+    __syncthreads();
+    copy_v(0, blk_v, v0);
+    int blk_k = 0;              // block ids of the tile whose K is copied next
+    if (N > 1) {
+        blk_v = key_block(1);
+        copy_k(1, blk_v, k1);
     }
+    blk_k = key_block(2);
+    auto no_dma = [](auto) {};
+    step(IC<2>{}, vl0, 0, kl0, 0, 0, no_dma);   // S of half 0
+    step(IC<6>{}, vl0, 0, kl0, 1, 0, no_dma);   // S of half 1; weights of half 0
 
+    auto iter = [&](auto par, int T) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par)::value;
+        uint8_t *vnxt = PAR ? v0 : v1, *knxt = PAR ? k1 : k0;   // V(T + 1), K(T + 2)
+        const uint8_t *vcur = PAR ? vl1 : vl0, *kcur = PAR ? kl0 : kl1;   // V(T), K(T + 1)
+        // the copies of V(T + 1) and K(T + 2), spread over the first step's
+        // slots (a burst of them would hold the wavefront's in-order issue
+        // behind the texture unit's queue); the second step covers their flight
+        constexpr int NCP = KPW + VPW, CPS = (NCP + NSLOT - 1) / NSLOT;
+        // (K(T + 2) past the last tile copies the last key again, into a
+        // buffer nothing reads: no branch in the slots)
+        auto dma = [&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            static_for<j * CPS, ((j + 1) * CPS < NCP ? (j + 1) * CPS : NCP)>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                if constexpr (q < KPW) copy_k_one(q, T + 2, blk_k, knxt);
+                else copy_v_one(q - KPW, T + 1, blk_v, vnxt);
+            });
+        };
+        __syncthreads();
+        step(IC<7>{}, vcur, 0, kcur, 0, 2 * T + 1, dma);
+        blk_v = blk_k;
+        blk_k = key_block(T + 3);
+        step(IC<7>{}, vcur, 1, kcur, 1, 2 * T + 2, no_dma);
+    };
+    auto last = [&](auto par) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par)::value;
+        const uint8_t *vcur = PAR ? vl1 : vl0;
+        __syncthreads();
+        zero_tail(N - 1, PAR ? v1 : v0);
+        __syncthreads();
+        step(IC<5>{}, vcur, 0, vcur, 0, 2 * N - 1, no_dma);   // P.V of half 2N-2; weights of half 2N-1
+        step(IC<1>{}, vcur, 1, vcur, 0, 2 * N, no_dma);       // P.V of half 2N-1
+    };
+    int T = 0;
+    for (; T + 2 <= N - 1; T += 2) {
+        iter(IC<0>{}, T);
+        iter(IC<1>{}, T + 1);
+    }
+    if (T < N - 1) {
+        iter(IC<0>{}, T);
+        last(IC<1>{});
+    } else {
+        last(IC<0>{});
+    }
     // normalise and store: lane holds row lrow, head-dim 32 dt + 8 (i / 4) + 4 half + i % 4
     if (!rvalid) return;
     const float lr = lsum + __shfl_xor(lsum, 32);   // both half-waves' keys
@@ -371,15 +543,15 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
         }
 }
 
-template <int DT>
+template <int DT, bool BUF>
 hipError_t launch_dt(const PrefixParams &p, int head_size, hipStream_t stream) {
     const dim3 grid((unsigned)((p.num_work + 7) / 8 * 8)), block(256);
     switch (head_size) {
-    case 64: hipLaunchKernelGGL((prefix_kernel<DT, 64>), grid, block, 0, stream, p); break;
-    case 96: hipLaunchKernelGGL((prefix_kernel<DT, 96>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((prefix_kernel<DT, 128>), grid, block, 0, stream, p); break;
-    case 192: hipLaunchKernelGGL((prefix_kernel<DT, 192>), grid, block, 0, stream, p); break;
-    case 256: hipLaunchKernelGGL((prefix_kernel<DT, 256>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((prefix_kernel<DT, 64, BUF>), grid, block, 0, stream, p); break;
+    case 96: hipLaunchKernelGGL((prefix_kernel<DT, 96, BUF>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((prefix_kernel<DT, 128, BUF>), grid, block, 0, stream, p); break;
+    case 192: hipLaunchKernelGGL((prefix_kernel<DT, 192, BUF>), grid, block, 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((prefix_kernel<DT, 256, BUF>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -394,7 +566,9 @@ bool prefix_mfma_supported(int dtype, int head_size, int bs_log2, float scale) {
 
 hipError_t launch_prefix(const PrefixParams &p, int dtype, int head_size, hipStream_t stream) {
     if (!prefix_mfma_supported(dtype, head_size, p.bs_log2, p.scale_log2)) return hipErrorInvalidValue;
-    return dtype == BF16 ? launch_dt<BF16>(p, head_size, stream) : launch_dt<F16>(p, head_size, stream);
+    if (p.offsets32)
+        return dtype == BF16 ? launch_dt<BF16, true>(p, head_size, stream) : launch_dt<F16, true>(p, head_size, stream);
+    return dtype == BF16 ? launch_dt<BF16, false>(p, head_size, stream) : launch_dt<F16, false>(p, head_size, stream);
 }
 
 }  // namespace pav2
