@@ -247,8 +247,16 @@ def prefix_bench(args, dev):
     out = torch.empty_like(pw.query)
     max_seq = max(a + b for a, b in zip(c["ctx"], c["ql"]))
     stream = torch.cuda.current_stream(dev)
+    # the key-range split's workspace, allocated once outside the timed region
+    ws_bytes = pav2.prefix_workspace_bytes(pw.query, pw.key_cache, pw.value_cache, pw.context_lens, max(c["ql"]),
+                                           max_seq)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    gqa = c["H"] // c["KVH"]
+    num_work = len(c["ctx"]) * c["KVH"] * -(-max(c["ql"]) * gqa // 128)
+    splits = ws_bytes // (num_work * 128 * (c["d"] + 2) * 4) if ws_bytes else 1
     fn = lambda: pav2.paged_prefix_attention(out, pw.query, pw.key_cache, pw.value_cache, pw.block_tables,
-                                             pw.query_start_loc, pw.context_lens, max(c["ql"]), max_seq)
+                                             pw.query_start_loc, pw.context_lens, max(c["ql"]), max_seq,
+                                             workspace=ws)
     mean, mn, wall = _time_launches(fn, args.steps, args.warmup, stream)
     flops = prefix_flops(c["ctx"], c["ql"], c["H"], c["d"])
     eb = 2 if c["dtype"] != "f32" else 4
@@ -263,6 +271,7 @@ def prefix_bench(args, dev):
                                "block 16", "num_seqs": 4, "context": 16384, "chunk": 512},
         "ms_min": round(mn, 5), "wall_ms_per_launch": round(wall, 5),
         "kv_GBps_if_read_once": round(kv_bytes / (mean * 1e-3) / 1e9, 1),
+        "key_range_splits": int(splits), "workspace_bytes": int(ws_bytes),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_prefix_traffic(),

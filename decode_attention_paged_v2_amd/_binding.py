@@ -74,6 +74,11 @@ def load():
         L.pav2_decode_kv.restype = I
         L.pav2_paged_prefix_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P]
         L.pav2_paged_prefix_attention.restype = I
+        L.pav2_paged_prefix_attention_ws.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P,
+                                                     ctypes.c_size_t, P]
+        L.pav2_paged_prefix_attention_ws.restype = I
+        L.pav2_prefix_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, F, I]
+        L.pav2_prefix_workspace_bytes.restype = ctypes.c_size_t
         L.pav2_reshape_and_cache.argtypes = [P, P, P, P, P, I, F, F, I, I, I, I, I, I, P]
         L.pav2_reshape_and_cache.restype = I
         L.pav2_read_stream.argtypes = [P, ctypes.c_int64, I, P, P]
@@ -318,12 +323,7 @@ def decode_kv(src, compute_dtype=None, stream=None):
     return dst.view(src.shape)
 
 
-def paged_prefix_attention(output, query, key_cache, value_cache, block_tables, query_start_loc,
-                           context_lens, max_query_len, max_seq_len, scale=None, stream=None) -> None:
-    """Paged prefix attention (pav2_paged_prefix_attention): the chunks' query
-    rows over their context plus the chunk itself (causal), all read from the
-    paged cache -- write the chunks' keys / values there first
-    (reshape_and_cache).  scale defaults to head_size ** -0.5."""
+def _prefix_args(output, query, key_cache, value_cache, block_tables, query_start_loc, context_lens, scale):
     T, H, D = (int(v) for v in query.shape)
     if tuple(output.shape) != (T, H, D) or output.dtype != query.dtype:
         raise ValueError("output must match query in shape and dtype")
@@ -336,11 +336,48 @@ def paged_prefix_attention(output, query, key_cache, value_cache, block_tables, 
     if int(query_start_loc.numel()) != S + 1 or int(block_tables.shape[0]) != S:
         raise ValueError("query_start_loc must be [num_seqs + 1] and block_tables [num_seqs, ...]")
     sc = float(D) ** -0.5 if scale is None else float(scale)
-    rc = load().pav2_paged_prefix_attention(
+    return S, H, KVH, D, bs, NB, sc
+
+
+def prefix_workspace_bytes(query, key_cache, value_cache, context_lens, max_query_len, max_seq_len,
+                           scale=None) -> int:
+    """Bytes of workspace paged_prefix_attention splits its key ranges with on
+    the current device (pav2_prefix_workspace_bytes); 0 when it would not."""
+    T, H, D = (int(v) for v in query.shape)
+    NB, KVH, bs = int(value_cache.shape[0]), int(value_cache.shape[1]), int(value_cache.shape[3])
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    return int(load().pav2_prefix_workspace_bytes(int(context_lens.numel()), H, KVH, D, bs, NB, int(max_query_len),
+                                                   int(max_seq_len), sc, _dtype_code(query)))
+
+
+def paged_prefix_attention(output, query, key_cache, value_cache, block_tables, query_start_loc,
+                           context_lens, max_query_len, max_seq_len, scale=None, stream=None,
+                           workspace="auto") -> None:
+    """Paged prefix attention (pav2_paged_prefix_attention_ws): the chunks'
+    query rows over their context plus the chunk itself (causal), all read
+    from the paged cache -- write the chunks' keys / values there first
+    (reshape_and_cache).  scale defaults to head_size ** -0.5.  workspace:
+    "auto" allocates what prefix_workspace_bytes asks for (torch's caching
+    allocator, so it follows the stream), None runs unsplit, or a uint8
+    device tensor of at least that size."""
+    import torch
+    S, H, KVH, D, bs, NB, sc = _prefix_args(output, query, key_cache, value_cache, block_tables, query_start_loc,
+                                            context_lens, scale)
+    ws, nbytes = None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a tensor')
+        nbytes = prefix_workspace_bytes(query, key_cache, value_cache, context_lens, max_query_len, max_seq_len, sc)
+        if nbytes:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=query.device)
+    elif workspace is not None:
+        ws, nbytes = workspace, int(workspace.numel()) * int(workspace.element_size())
+    rc = load().pav2_paged_prefix_attention_ws(
         _dev(output, "output"), _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
         _i32(block_tables, "block_tables"), _i32(query_start_loc, "query_start_loc"),
         _i32(context_lens, "context_lens"), S, H, KVH, D, bs, NB, int(block_tables.shape[1]), int(max_query_len),
-        int(max_seq_len), sc, _dtype_code(query), _stream(query, stream))
+        int(max_seq_len), sc, _dtype_code(query), _dev(ws, "workspace") if ws is not None else None, nbytes,
+        _stream(query, stream))
     _check(rc)
 
 

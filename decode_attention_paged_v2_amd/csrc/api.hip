@@ -547,12 +547,38 @@ int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype
                          "decode_kv");
 }
 
-int pav2_paged_prefix_attention(void *output, const void *query, const void *key_cache,
-                                const void *value_cache, const int32_t *block_tables,
-                                const int32_t *query_start_loc, const int32_t *context_lens, int num_seqs,
-                                int num_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,
-                                int max_blocks_per_seq, int max_query_len, int max_seq_len, float scale,
-                                pav2_dtype_t dtype, pav2_stream_t stream) {
+namespace {
+
+// The MFMA prefix kernel's work count and key-range split for a call (the
+// same on the workspace query and the call): 0 when the call does not take
+// that kernel.
+struct PrefixPlan {
+    bool mfma = false;
+    int64_t row_blocks = 0, work = 0;
+    bool offsets32 = false;
+    int splits = 1;
+};
+
+PrefixPlan plan_prefix(int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,
+                       int max_query_len, int max_seq_len, float scale, pav2_dtype_t dtype) {
+    PrefixPlan pl;
+    const int gqa = num_heads / num_kv_heads;
+    pl.mfma = pav2::prefix_mfma_supported((int)dtype, head_size, ilog2_exact(block_size), scale);
+    const int rows_per_wg = pl.mfma ? pav2::kPrefixMfmaRows : pav2::kPrefixRows;
+    pl.row_blocks = ((int64_t)max_query_len * gqa + rows_per_wg - 1) / rows_per_wg;
+    pl.work = (int64_t)num_seqs * num_kv_heads * pl.row_blocks;
+    if (pl.mfma) {
+        const int64_t blk_stride = (int64_t)head_size * block_size * elem_bytes(dtype) * num_kv_heads;
+        pl.offsets32 = (int64_t)num_blocks * blk_stride <= ((int64_t)1 << 32);
+    }
+    return pl;
+}
+
+int prefix_impl(void *output, const void *query, const void *key_cache, const void *value_cache,
+                const int32_t *block_tables, const int32_t *query_start_loc, const int32_t *context_lens,
+                int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,
+                int max_blocks_per_seq, int max_query_len, int max_seq_len, float scale, pav2_dtype_t dtype,
+                void *workspace, size_t workspace_bytes, pav2_stream_t stream) {
     g_err[0] = 0;
     if (dtype == PAV2_FP8_E4M3)
         return fail(PAV2_ERR_UNSUPPORTED, "prefix attention takes f32, f16 or bf16 caches of the query dtype");
@@ -565,10 +591,10 @@ int pav2_paged_prefix_attention(void *output, const void *query, const void *key
     int rc = check_shape(sh);
     if (rc) return rc;
     const int gqa = num_heads / num_kv_heads;
-    const bool mfma = pav2::prefix_mfma_supported((int)dtype, head_size, ilog2_exact(block_size), scale);
-    const int rows_per_wg = mfma ? pav2::kPrefixMfmaRows : pav2::kPrefixRows;
-    const int64_t row_blocks = ((int64_t)max_query_len * gqa + rows_per_wg - 1) / rows_per_wg;
-    const int64_t work = (int64_t)num_seqs * num_kv_heads * row_blocks;
+    const PrefixPlan pl = plan_prefix(num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                      max_query_len, max_seq_len, scale, dtype);
+    const bool mfma = pl.mfma;
+    const int64_t row_blocks = pl.row_blocks, work = pl.work;
     if (work > ((int64_t)1 << 31) - 1 || row_blocks > ((int64_t)1 << 30))
         return fail(PAV2_ERR_UNSUPPORTED, "num_seqs * num_kv_heads * row blocks = %lld is too large", (long long)work);
     if (work == 0) return PAV2_OK;
@@ -594,7 +620,16 @@ int pav2_paged_prefix_attention(void *output, const void *query, const void *key
         q.head_stride = (int64_t)head_size * block_size * elem_bytes(dtype);
         q.blk_stride = q.head_stride * num_kv_heads;
         q.scale_log2 = scale * 1.4426950408889634f;
-        q.offsets32 = (int64_t)num_blocks * q.blk_stride <= ((int64_t)1 << 32);
+        q.offsets32 = pl.offsets32;
+        if (workspace) {   // split the key ranges when the workspace holds the partials
+            const int sp = work * pav2::kPrefixMaxSplits > ((int64_t)1 << 31) - 1
+                               ? 1
+                               : pav2::prefix_splits((int)dtype, head_size, q.offsets32, (int)work, max_seq_len);
+            if (sp > 1 && workspace_bytes >= pav2::prefix_workspace_bytes(sp, (int)work, head_size)) {
+                q.splits = sp;
+                q.part = static_cast<float *>(workspace);
+            }
+        }
         return launch_status(pav2::launch_prefix(q, (int)dtype, head_size, static_cast<hipStream_t>(stream)),
                              "prefix attention");
     }
@@ -629,6 +664,46 @@ int pav2_paged_prefix_attention(void *output, const void *query, const void *key
     return launch_status(pav2::launch_phase1(p, (int)dtype, (int)dtype, head_size, pav2::kPhase1Waves, lds,
                                              static_cast<hipStream_t>(stream)),
                          "prefix attention");
+}
+
+}  // namespace
+
+int pav2_paged_prefix_attention(void *output, const void *query, const void *key_cache,
+                                const void *value_cache, const int32_t *block_tables,
+                                const int32_t *query_start_loc, const int32_t *context_lens, int num_seqs,
+                                int num_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_query_len, int max_seq_len, float scale,
+                                pav2_dtype_t dtype, pav2_stream_t stream) {
+    return prefix_impl(output, query, key_cache, value_cache, block_tables, query_start_loc, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_size, block_size, num_blocks, max_blocks_per_seq, max_query_len,
+                       max_seq_len, scale, dtype, nullptr, 0, stream);
+}
+
+int pav2_paged_prefix_attention_ws(void *output, const void *query, const void *key_cache,
+                                   const void *value_cache, const int32_t *block_tables,
+                                   const int32_t *query_start_loc, const int32_t *context_lens, int num_seqs,
+                                   int num_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,
+                                   int max_blocks_per_seq, int max_query_len, int max_seq_len, float scale,
+                                   pav2_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                   pav2_stream_t stream) {
+    return prefix_impl(output, query, key_cache, value_cache, block_tables, query_start_loc, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_size, block_size, num_blocks, max_blocks_per_seq, max_query_len,
+                       max_seq_len, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t pav2_prefix_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+                                   int num_blocks, int max_query_len, int max_seq_len, float scale,
+                                   pav2_dtype_t dtype) {
+    g_err[0] = 0;
+    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_size <= 0 ||
+        block_size <= 0 || (block_size & (block_size - 1)) || num_blocks <= 0 || max_query_len <= 0 ||
+        max_seq_len < max_query_len || dtype == PAV2_FP8_E4M3)
+        return 0;
+    const PrefixPlan pl = plan_prefix(num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                      max_query_len, max_seq_len, scale, dtype);
+    if (!pl.mfma || pl.work <= 0 || pl.work * pav2::kPrefixMaxSplits > ((int64_t)1 << 31) - 1) return 0;
+    const int sp = pav2::prefix_splits((int)dtype, head_size, pl.offsets32, (int)pl.work, max_seq_len);
+    return pav2::prefix_workspace_bytes(sp, (int)pl.work, head_size);
 }
 
 int pav2_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,

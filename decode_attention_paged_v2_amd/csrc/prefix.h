@@ -24,6 +24,11 @@ struct PrefixParams {
     // first block (num_blocks * blk_stride <= 2^32): the tiles are then copied
     // with buffer (32-bit offset) loads into LDS, else with global ones
     bool offsets32;
+    // key ranges per row block: 1 writes the output directly; more split each
+    // row block's tiles into that many ranges whose normalised partial
+    // outputs (float32) and statistics go to `part`, merged by a second kernel
+    int splits = 1;
+    float *part = nullptr;           // [splits * num_work * 128] x (D + 2) floats: o, then m, then l
 };
 
 constexpr int kPrefixMfmaRows = 128;   // query rows per workgroup
@@ -32,6 +37,13 @@ constexpr int kPrefixMfmaRows = 128;   // query rows per workgroup
 // multiple of 32, blocks of at least 8 tokens, a positive scale); others take
 // phase 1's prefix schedule.
 bool prefix_mfma_supported(int dtype, int head_size, int bs_log2, float scale);
+// Key ranges per row block (1 .. kPrefixMaxSplits) that balance this launch
+// over the current device's compute units, from the kernel's occupancy; 1
+// when splitting does not shorten the estimated run.
+constexpr int kPrefixMaxSplits = 8;
+int prefix_splits(int dtype, int head_size, bool offsets32, int num_work, int max_seq_len);
+// Workspace bytes for `splits` ranges (0 for one).
+size_t prefix_workspace_bytes(int splits, int num_work, int head_size);
 hipError_t launch_prefix(const PrefixParams &p, int dtype, int head_size, hipStream_t stream);
 
 }  // namespace pav2

@@ -38,6 +38,10 @@
 //   weights the MFMAs saw.
 #include <math.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "pav2_internal.h"
 #include "prefix.h"
 
@@ -130,8 +134,9 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
 
     // workgroups numbered XCD by XCD (grid a multiple of 8; blockIdx % 8 picks
     // the XCD), so the row blocks of one (sequence, kv head) share an L2
-    const int wg = (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3));
-    if (wg >= P.num_work) return;
+    const int item = (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3));
+    if (item >= P.num_work * P.splits) return;
+    const int split = item / P.num_work, wg = item - split * P.num_work;   // key range, row block
     const int RB = P.row_blocks, KVH = P.num_kv_heads, gqa = P.gqa;
     const int s = wg / (KVH * RB), g = (wg / RB) % KVH, rb = wg % RB;
     const int q0 = P.query_start_loc[s];
@@ -141,6 +146,9 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
     const int Lmax = ctx + (min(nrows, (rb + 1) * kRows) - 1) / gqa + 1;   // the block's largest limit
     const int lmin = ctx + (rb * kRows) / gqa + 1;                          // its smallest
     const int ntiles = (Lmax + kKeys - 1) / kKeys;
+    // this item's tiles [tb, te): range `split` of the row block's
+    const int tper = (ntiles + P.splits - 1) / P.splits;
+    const int tb = split * tper, te = min(ntiles, tb + tper);
 
     // this lane's query row and its causal limit (keys t < lim)
     const int row = rb * kRows + wv * 32 + lrow;
@@ -467,21 +475,20 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
     // it finds its tiles landed and those buffers free.  K runs one tile
     // ahead of V.  Iterations come in pairs (static buffer choice, no exit
     // between them), then the last tile's P.V.
-    const int N = ntiles;
-    int blk_v = key_block(0);   // block ids of the tile whose V is copied next
-    __syncthreads();            // the zeroed tiles are in place before any copy lands
-    copy_k(0, blk_v, k0);
-    __syncthreads();
-    copy_v(0, blk_v, v0);
+    int blk_v = key_block(tb);  // block ids of the tile whose V is copied next
     int blk_k = 0;              // block ids of the tile whose K is copied next
-    if (N > 1) {
-        blk_v = key_block(1);
-        copy_k(1, blk_v, k1);
-    }
-    blk_k = key_block(2);
     auto no_dma = [](auto) {};
-    step(IC<2>{}, vl0, 0, kl0, 0, 0, no_dma);   // S of half 0
-    step(IC<6>{}, vl0, 0, kl0, 1, 0, no_dma);   // S of half 1; weights of half 0
+    if (tb < te) {
+        __syncthreads();   // the zeroed tiles are in place before any copy lands
+        copy_k(tb, blk_v, k0);
+        __syncthreads();
+        copy_v(tb, blk_v, v0);
+        blk_v = key_block(tb + 1);
+        copy_k(tb + 1, blk_v, k1);   // (past the range: a buffer nothing reads)
+        blk_k = key_block(tb + 2);
+        step(IC<2>{}, vl0, 0, kl0, 0, 2 * tb, no_dma);       // S of the range's first half
+        step(IC<6>{}, vl0, 0, kl0, 1, 2 * tb, no_dma);       // S of its second; weights of the first
+    }
 
     auto iter = [&](auto par, int T) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par)::value;
@@ -511,26 +518,46 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
         constexpr int PAR = decltype(par)::value;
         const uint8_t *vcur = PAR ? vl1 : vl0;
         __syncthreads();
-        zero_tail(N - 1, PAR ? v1 : v0);
+        zero_tail(te - 1, PAR ? v1 : v0);
         __syncthreads();
-        step(IC<5>{}, vcur, 0, vcur, 0, 2 * N - 1, no_dma);   // P.V of half 2N-2; weights of half 2N-1
-        step(IC<1>{}, vcur, 1, vcur, 0, 2 * N, no_dma);       // P.V of half 2N-1
+        step(IC<5>{}, vcur, 0, vcur, 0, 2 * te - 1, no_dma);   // P.V of half 2te-2; weights of half 2te-1
+        step(IC<1>{}, vcur, 1, vcur, 0, 2 * te, no_dma);       // P.V of half 2te-1
     };
-    int T = 0;
-    for (; T + 2 <= N - 1; T += 2) {
-        iter(IC<0>{}, T);
-        iter(IC<1>{}, T + 1);
-    }
-    if (T < N - 1) {
-        iter(IC<0>{}, T);
-        last(IC<1>{});
-    } else {
-        last(IC<0>{});
+    if (tb < te) {
+        int T = tb;
+        for (; T + 2 <= te - 1; T += 2) {
+            iter(IC<0>{}, T);
+            iter(IC<1>{}, T + 1);
+        }
+        if (T < te - 1) {
+            iter(IC<0>{}, T);
+            last(IC<1>{});
+        } else {
+            last(IC<0>{});
+        }
     }
     // normalise and store: lane holds row lrow, head-dim 32 dt + 8 (i / 4) + 4 half + i % 4
     if (!rvalid) return;
     const float lr = lsum + __shfl_xor(lsum, 32);   // both half-waves' keys
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+    if (P.splits > 1) {   // a partial over tiles [tb, te): o / l, the offset m and l, in float32
+        const int64_t pi = ((int64_t)(split * P.num_work + wg) * kRows) + wv * 32 + lrow;
+        float *po = P.part + pi * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int d = 32 * dt + 8 * q + 4 * half;
+                *reinterpret_cast<float4 *>(po + d) = make_float4(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv,
+                                                                  o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
+            }
+        if (half == 0) {
+            const int64_t np = (int64_t)P.splits * P.num_work * kRows;
+            P.part[np * D + pi] = lr > 0.0f ? m_used : -INFINITY;
+            P.part[np * (D + 1) + pi] = lr;
+        }
+        return;
+    }
     uint8_t *orow = reinterpret_cast<uint8_t *>(P.out) + ((int64_t)(q0 + jq) * P.num_heads + g * gqa + rq) * D * 2;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -543,18 +570,113 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
         }
 }
 
+// The merge of a row block's key ranges: out = sum_c w_c o_c / sum_c w_c with
+// w_c = l_c 2^(m_c - M), M = max_c m_c (each o_c already divided by l_c), the
+// online softmax's combination of partial results over disjoint key sets.
+template <int DT, int D>
+__global__ void __launch_bounds__(256) prefix_merge_kernel(const PrefixParams P) {
+    constexpr int RPB = 16;   // rows per workgroup: 16 threads per row, each a float4 column stride 16
+    const int wg = blockIdx.x / (kRows / RPB), rr = (blockIdx.x % (kRows / RPB)) * RPB + (threadIdx.x >> 4);
+    const int RB = P.row_blocks, KVH = P.num_kv_heads, gqa = P.gqa;
+    const int s = wg / (KVH * RB), g = (wg / RB) % KVH, rb = wg % RB;
+    const int q0 = P.query_start_loc[s];
+    const int nrows = (P.query_start_loc[s + 1] - q0) * gqa;
+    const int row = rb * kRows + rr;
+    if (row >= nrows) return;
+    const int64_t np = (int64_t)P.splits * P.num_work * kRows;
+    float M = -INFINITY;
+    for (int c = 0; c < P.splits; ++c) M = fmaxf(M, P.part[np * D + (int64_t)(c * P.num_work + wg) * kRows + rr]);
+    float wc[kPrefixMaxSplits];
+    float W = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kPrefixMaxSplits; ++c) {
+        wc[c] = 0.0f;
+        if (c < P.splits) {
+            const int64_t pi = (int64_t)(c * P.num_work + wg) * kRows + rr;
+            const float l = P.part[np * (D + 1) + pi];
+            if (l > 0.0f) wc[c] = l * exp2f(P.part[np * D + pi] - M);   // (a range with no visible key: 0)
+            W += wc[c];
+        }
+    }
+    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+    const int jq = row / gqa, rq = row - jq * gqa;
+    uint8_t *orow = reinterpret_cast<uint8_t *>(P.out) + ((int64_t)(q0 + jq) * P.num_heads + g * gqa + rq) * D * 2;
+#pragma unroll
+    for (int k = 0; k < (D / 4 + 15) / 16; ++k) {
+        const int c4 = (threadIdx.x & 15) + 16 * k;
+        if (c4 >= D / 4) break;
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kPrefixMaxSplits; ++c) {
+            if (c < P.splits && wc[c] > 0.0f) {
+                const int64_t pi = (int64_t)(c * P.num_work + wg) * kRows + rr;
+                const float4 v = *reinterpret_cast<const float4 *>(P.part + pi * D + 4 * c4);
+                a0 = fmaf(wc[c], v.x, a0);
+                a1 = fmaf(wc[c], v.y, a1);
+                a2 = fmaf(wc[c], v.z, a2);
+                a3 = fmaf(wc[c], v.w, a3);
+            }
+        }
+        *reinterpret_cast<u32x2 *>(orow + 8 * c4) = u32x2{pack16<DT>(a0 * inv, a1 * inv), pack16<DT>(a2 * inv, a3 * inv)};
+    }
+}
+
+template <int DT, bool BUF, int D>
+hipError_t launch_d(const PrefixParams &p, hipStream_t stream) {
+    const dim3 grid((unsigned)(((int64_t)p.num_work * p.splits + 7) / 8 * 8)), block(256);
+    hipLaunchKernelGGL((prefix_kernel<DT, D, BUF>), grid, block, 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    hipLaunchKernelGGL((prefix_merge_kernel<DT, D>), dim3((unsigned)p.num_work * (kRows / 16)), block, 0, stream, p);
+    return hipGetLastError();
+}
+
 template <int DT, bool BUF>
 hipError_t launch_dt(const PrefixParams &p, int head_size, hipStream_t stream) {
-    const dim3 grid((unsigned)((p.num_work + 7) / 8 * 8)), block(256);
     switch (head_size) {
-    case 64: hipLaunchKernelGGL((prefix_kernel<DT, 64, BUF>), grid, block, 0, stream, p); break;
-    case 96: hipLaunchKernelGGL((prefix_kernel<DT, 96, BUF>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((prefix_kernel<DT, 128, BUF>), grid, block, 0, stream, p); break;
-    case 192: hipLaunchKernelGGL((prefix_kernel<DT, 192, BUF>), grid, block, 0, stream, p); break;
-    case 256: hipLaunchKernelGGL((prefix_kernel<DT, 256, BUF>), grid, block, 0, stream, p); break;
+    case 64: return launch_d<DT, BUF, 64>(p, stream);
+    case 96: return launch_d<DT, BUF, 96>(p, stream);
+    case 128: return launch_d<DT, BUF, 128>(p, stream);
+    case 192: return launch_d<DT, BUF, 192>(p, stream);
+    case 256: return launch_d<DT, BUF, 256>(p, stream);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+}
+
+// the attention kernel of a case, for occupancy queries
+const void *kernel_of(int dtype, int head_size, bool buf) {
+#define PAV2_PREFIX_K(DT, D)                                                                                   \
+    (buf ? reinterpret_cast<const void *>(&prefix_kernel<DT, D, true>)                                      \
+         : reinterpret_cast<const void *>(&prefix_kernel<DT, D, false>))
+    const bool bf = dtype == BF16;
+    switch (head_size) {
+    case 64: return bf ? PAV2_PREFIX_K(BF16, 64) : PAV2_PREFIX_K(F16, 64);
+    case 96: return bf ? PAV2_PREFIX_K(BF16, 96) : PAV2_PREFIX_K(F16, 96);
+    case 128: return bf ? PAV2_PREFIX_K(BF16, 128) : PAV2_PREFIX_K(F16, 128);
+    case 192: return bf ? PAV2_PREFIX_K(BF16, 192) : PAV2_PREFIX_K(F16, 192);
+    case 256: return bf ? PAV2_PREFIX_K(BF16, 256) : PAV2_PREFIX_K(F16, 256);
+    default: return nullptr;
+    }
+#undef PAV2_PREFIX_K
+}
+
+// concurrent workgroups of a kernel on the current device (occupancy x CUs),
+// queried once per (device, kernel)
+int resident_slots(const void *kern) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({dev, kern});
+    if (it != cache.end()) return it->second;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int slots = per_cu * cus;
+    cache[{dev, kern}] = slots;
+    return slots;
 }
 
 }  // namespace
@@ -564,8 +686,31 @@ bool prefix_mfma_supported(int dtype, int head_size, int bs_log2, float scale) {
            scale > 0.0f;
 }
 
+int prefix_splits(int dtype, int head_size, bool offsets32, int num_work, int max_seq_len) {
+    const void *kern = kernel_of(dtype, head_size, offsets32);
+    const int slots = kern ? resident_slots(kern) : 0;
+    if (slots <= 0 || num_work <= 0) return 1;
+    // estimated run: rounds of resident workgroups x tiles per range, plus a
+    // tile's worth for writing and merging the partials; ranges of >= 4 tiles
+    const int64_t tiles = ((int64_t)max_seq_len + kKeys - 1) / kKeys;
+    auto cost = [&](int sp) {
+        const int64_t rounds = ((int64_t)num_work * sp + slots - 1) / slots;
+        return rounds * ((tiles + sp - 1) / sp) + (sp > 1 ? 2 : 0);
+    };
+    int best = 1;
+    for (int sp = 2; sp <= kPrefixMaxSplits && (tiles + sp - 1) / sp >= 4; ++sp)
+        if (cost(sp) < cost(best)) best = sp;
+    return best;
+}
+
+size_t prefix_workspace_bytes(int splits, int num_work, int head_size) {
+    if (splits <= 1) return 0;
+    return (size_t)splits * (size_t)num_work * kRows * (size_t)(head_size + 2) * sizeof(float);
+}
+
 hipError_t launch_prefix(const PrefixParams &p, int dtype, int head_size, hipStream_t stream) {
     if (!prefix_mfma_supported(dtype, head_size, p.bs_log2, p.scale_log2)) return hipErrorInvalidValue;
+    if (p.splits < 1 || p.splits > kPrefixMaxSplits || (p.splits > 1 && !p.part)) return hipErrorInvalidValue;
     if (p.offsets32)
         return dtype == BF16 ? launch_dt<BF16, true>(p, head_size, stream) : launch_dt<F16, true>(p, head_size, stream);
     return dtype == BF16 ? launch_dt<BF16, false>(p, head_size, stream) : launch_dt<F16, false>(p, head_size, stream);

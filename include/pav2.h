@@ -324,10 +324,13 @@ int pav2_decode_kv(const void *src, float *dst, int64_t n, pav2_dtype_t kv_dtype
  *
  * max_query_len >= every chunk's length and max_seq_len >= every context +
  * chunk length (host values sizing the grid and validating the table width).
- * One workgroup per (sequence, kv head, 64 (token, head) rows): its four
- * wavefronts hold 16 rows each and walk the same 512-token key slices up to
- * their rows' causal limits with a running softmax.
+ * f16 / bf16 with head sizes 64, 96, 128, 192 or 256, blocks of >= 8 tokens
+ * and scale > 0 run on MFMA tiles: one workgroup per (sequence, kv head, 128
+ * (token, head) rows), the kv head's keys streamed through LDS 64 at a time
+ * with a running softmax.  Other cases (f32, other head sizes, blocks of 1,
+ * 2 or 4 tokens) run a vector kernel of 64 rows per workgroup.
  * No ALiBi or sliding window (the page's fallback applies neither).
+ * Returns 0, or a negative status with pav2_last_error() set.
  */
 int pav2_paged_prefix_attention(
     void *output, const void *query, const void *key_cache, const void *value_cache,
@@ -335,6 +338,37 @@ int pav2_paged_prefix_attention(
     int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
     int num_blocks, int max_blocks_per_seq, int max_query_len, int max_seq_len,
     float scale, pav2_dtype_t dtype, pav2_stream_t stream);
+
+/*
+ * pav2_paged_prefix_attention with a caller-owned device workspace that lets
+ * the MFMA path split each row block's keys into up to 8 contiguous ranges
+ * when too few workgroups would fill the device's compute units (each range
+ * computes a partial softmax result in float32; a second kernel combines
+ * them as the online softmax combines disjoint key sets: the same quantity
+ * as the unsplit call, up to float32 rounding).  workspace holds at least
+ * pav2_prefix_workspace_bytes(...) bytes for these arguments on the current
+ * device, aligned to 16 bytes, and is not read before it is written; a NULL
+ * or smaller workspace runs the call unsplit.  It is in use until the call's
+ * work on `stream` completes: calls that may overlap need their own.
+ */
+int pav2_paged_prefix_attention_ws(
+    void *output, const void *query, const void *key_cache, const void *value_cache,
+    const int32_t *block_tables, const int32_t *query_start_loc, const int32_t *context_lens,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+    int num_blocks, int max_blocks_per_seq, int max_query_len, int max_seq_len,
+    float scale, pav2_dtype_t dtype, void *workspace, size_t workspace_bytes,
+    pav2_stream_t stream);
+
+/*
+ * Workspace bytes pav2_paged_prefix_attention_ws uses for these arguments on
+ * the current device: 0 when the call would not split (or its arguments are
+ * invalid; the call itself reports those).  The split count comes from the
+ * kernel's occupancy and the device's compute-unit count, so the figure is
+ * per device model.
+ */
+size_t pav2_prefix_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                   int block_size, int num_blocks, int max_query_len, int max_seq_len,
+                                   float scale, pav2_dtype_t dtype);
 
 /*
  * KV-cache write (page "paged_attn.py", write_to_paged_cache, which passes

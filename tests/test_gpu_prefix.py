@@ -105,6 +105,59 @@ def test_prefix_one_token_chunks_match_decode_oracle():
     assert_close(out.cpu(), ref, "bf16")
 
 
+def _prefix_call(g, ql, ctx, scale, workspace):
+    out = torch.full_like(g.query, float("nan"))
+    pav2.paged_prefix_attention(out, g.query, g.key_cache, g.value_cache, g.block_tables, g.query_start_loc,
+                                g.context_lens, max(ql), max(c + q for c, q in zip(ctx, ql)), scale=scale,
+                                workspace=workspace)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+@pytest.mark.parametrize("dtype,d,ctx,ql,H,KVH", [
+    ("bf16", 256, [3000], [40], 8, 1),               # 3 row blocks over 48 tiles: 8 key ranges
+    ("f16", 128, [2100, 0, 64, 900], [30, 50, 1, 7], 12, 4),   # ragged: empty ranges, rows before a range
+    ("bf16", 64, [5000, 40], [3, 90], 16, 2),
+])
+def test_prefix_key_ranges_split(dtype, d, ctx, ql, H, KVH):
+    """Few row blocks over long contexts: the call splits each row block's keys
+    into ranges merged afterwards.  The split result matches the oracle, the
+    unsplit call (workspace None) matches it too, and the two agree to float32
+    rounding of the merge."""
+    print(f"case prefix split {dtype} d={d} ctx={ctx}", flush=True)
+    pw = W.prefix_workload(ctx, ql, H, KVH, d, 16, dtype=dtype, seed=d + len(ctx))
+    scale = d ** -0.5
+    ref = oracle.prefix_attention(pw.query, pw.key, pw.value, pw.key_cache, pw.value_cache, pw.block_tables,
+                                  pw.query_start_loc, pw.context_lens, num_kv_heads=KVH, block_size=16,
+                                  scale=scale, q_dtype=_CODE[dtype], kv_dtype=_CODE[dtype])
+    g = pw.to(DEV)
+    pav2.reshape_and_cache(g.key, g.value, g.key_cache, g.value_cache, g.slot_mapping)
+    max_seq = max(c + q for c, q in zip(ctx, ql))
+    assert pav2.prefix_workspace_bytes(g.query, g.key_cache, g.value_cache, g.context_lens, max(ql), max_seq,
+                                       scale) > 0
+    split = _prefix_call(g, ql, ctx, scale, "auto")
+    whole = _prefix_call(g, ql, ctx, scale, None)
+    assert_close(split, ref, dtype)
+    assert_close(whole, ref, dtype)
+    # both are the output dtype's rounding of nearly the same float32 value
+    diff = (split.double() - whole.double()).abs().max().item()
+    assert diff <= 2 * _tol.ulp(np.abs(whole.double().numpy()).max(), _TD[dtype]), diff
+
+
+def test_prefix_small_workspace_runs_unsplit():
+    """A workspace below the query's size is not used: the result is the unsplit call's, bit for bit."""
+    ctx, ql = [3000], [40]
+    pw = W.prefix_workload(ctx, ql, 8, 1, 128, 16, dtype="bf16", seed=3)
+    g = pw.to(DEV)
+    pav2.reshape_and_cache(g.key, g.value, g.key_cache, g.value_cache, g.slot_mapping)
+    need = pav2.prefix_workspace_bytes(g.query, g.key_cache, g.value_cache, g.context_lens, 40, 3040)
+    assert need > 0
+    small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    a = _prefix_call(g, ql, ctx, None, small)
+    b = _prefix_call(g, ql, ctx, None, None)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_prefix_rejects_fp8_cache():
     pw = W.prefix_workload([4], [2], 4, 4, 64, 16, dtype="bf16").to(DEV)
     kc = pw.key_cache.to(torch.float8_e4m3fn)
