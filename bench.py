@@ -231,7 +231,7 @@ def measured_prefix_traffic():
         return None
     with open(path) as fh:
         data = json.load(fh)
-    if data.get("source_hash") != rocprof_harness.source_hash() or "traffic_bytes" not in data:
+    if data.get("source_hash") != rocprof_harness.source_hash("prefix") or "traffic_bytes" not in data:
         return None
     return round(float(data["traffic_bytes"]))
 
@@ -275,7 +275,8 @@ def prefix_bench(args, dev):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_prefix_traffic(),
-                     "kernel": "phase1_kernel (prefix)", "algorithmic_flops_per_launch": flops},
+                     "kernel": "prefix_kernel (+ prefix_merge_kernel when split: the call's time)",
+                     "algorithmic_flops_per_launch": flops},
         "library": pav2.lib_path(),
     }
     if not args.no_cpu_baseline:

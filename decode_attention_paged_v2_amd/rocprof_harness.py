@@ -43,8 +43,8 @@ BENCH = os.path.join(ROOT, "bench.py")
 _PLAN = [os.path.join(HERE, "csrc", "api.hip"), os.path.join(ROOT, "include", "pav2.h")]
 KERNEL_SOURCES = {
     "decode": sorted(glob.glob(os.path.join(HERE, "csrc", "phase1*"))) +
-              [os.path.join(HERE, "csrc", f) for f in ("phase2.hip", "pav2_internal.h", "prefix.hip", "prefix.h")]
-              + _PLAN,
+              [os.path.join(HERE, "csrc", f) for f in ("phase2.hip", "pav2_internal.h")] + _PLAN,
+    "prefix": [os.path.join(HERE, "csrc", f) for f in ("prefix.hip", "prefix.h", "pav2_internal.h")] + _PLAN,
     "cache_write": [os.path.join(HERE, "csrc", f) for f in ("cache.hip", "cache.h", "pav2_internal.h")] + _PLAN,
 }
 
@@ -84,6 +84,10 @@ def _csv(pattern):
 
 
 def _kind(name: str) -> str:
+    if "prefix_merge_kernel" in name:
+        return "prefix_merge"
+    if "prefix_kernel" in name:
+        return "prefix"
     if "phase1_kernel" in name:
         return "phase1"
     if "phase2_kernel" in name:
@@ -145,7 +149,7 @@ def pmc(config: str, out: str, mode: str = "decode", entry: str = "v2") -> dict:
     """FETCH_SIZE and WRITE_SIZE per launch of the profiled kernels, scaled by the copy reference."""
     res = {}
     # the single-pass entry point launches the phase-1 kernel template only
-    kinds = {"cache_write": ("cache_write",), "prefix": ("phase1",)}.get(
+    kinds = {"cache_write": ("cache_write",), "prefix": ("prefix", "prefix_merge")}.get(
         mode, ("phase1",) if entry == "v1" else ("phase1", "phase2"))
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         for what in (config, "copy"):
@@ -168,6 +172,9 @@ def pmc(config: str, out: str, mode: str = "decode", entry: str = "v2") -> dict:
                 for k in kinds:
                     # dispatches of the largest grid (the cache write also times a decode step)
                     mine = [r for r in rows if _kind(r["Kernel_Name"]) == k]
+                    if not mine:   # (an unsplit prefix call launches no merge)
+                        res[f"{counter}_{k}_kib"] = 0.0
+                        continue
                     top = max(int(r["Grid_Size"]) for r in mine)
                     vals = [float(r["Counter_Value"]) for r in mine if int(r["Grid_Size"]) == top]
                     res[f"{counter}_{k}_kib"] = sum(vals) / len(vals)
@@ -345,6 +352,20 @@ def write_cache_summary(config: str, out: str, trace: dict, counters: dict | Non
     return os.path.join(out, name + ".md")
 
 
+def _bench_json(log: str) -> dict:
+    """The bench's JSON line from a profiled run's log (the last line that parses); {} without one."""
+    if not os.path.exists(log):
+        return {}
+    with open(log) as fh:
+        for line in reversed(fh.read().splitlines()):
+            if line.startswith("{"):
+                try:
+                    return json.loads(line)
+                except ValueError:
+                    continue
+    return {}
+
+
 def write_prefix_summary(out: str, trace: dict, counters: dict | None = None) -> str:
     import importlib.util
     spec = importlib.util.spec_from_file_location("bench_for_counts", BENCH)
@@ -352,44 +373,62 @@ def write_prefix_summary(out: str, trace: dict, counters: dict | None = None) ->
     spec.loader.exec_module(bench)
     c = bench.PREFIX_CASE
     flops = bench.prefix_flops(c["ctx"], c["ql"], c["H"], c["d"])
-    t = trace["phase1"]
+    t, tm = trace["prefix"], trace.get("prefix_merge")
+    line = _bench_json(os.path.join(out, "trace_prefix.log"))
+    splits, ws = line.get("key_range_splits", 1), line.get("workspace_bytes", 0)
+    call_us = t["avg_us"] + (tm["avg_us"] if tm else 0.0)
     tf = flops / (t["avg_us"] * 1e-6) / 1e12
+    tf_call = flops / (call_us * 1e-6) / 1e12
     name = "prefix_attention"
     lines = ["# Paged prefix attention profile: 4 seqs x (16384 cached + 512 new tokens), H=24, kv_h=4, d=256, bf16",
-             "", f"Kernel sources hash: `{source_hash('decode')}`", "",
+             "", f"Kernel sources hash: `{source_hash('prefix')}`", "",
              "Command (from the repository root):", "",
              "    python -m decode_attention_paged_v2_amd.rocprof_harness --mode prefix --out gpurun_out/prof"
              + (" --pmc" if counters else ""), "",
              "which runs:", "", "    " + trace["command"], "",
-             "| kernel | calls | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|",
-             f"| `{t['name'][:90]}` | {t['calls']} | {t['avg_us']:.2f} | {t['min_us']:.2f} | {t['max_us']:.2f} |", "",
-             f"Algorithmic flops per launch (4 d per visible (row, key) pair): {flops:,}; at the average duration "
-             f"that is {tf:.1f} TFLOP/s = {100 * tf / 2500:.2f} % of the 2.5 PFLOP/s bf16 MFMA peak."]
-    data = {"source_hash": source_hash("decode"), "trace": trace, "algorithmic_flops": flops, "achieved_TFLOPs": tf,
-            "taken": time.strftime("%Y-%m-%d %H:%M:%S")}
+             f"Key ranges per row block: {splits} (workspace {ws:,} bytes); the call is the attention kernel "
+             "and, when split, the merge kernel.", "",
+             "| kernel | calls | average (µs) | min (µs) | max (µs) |", "|---|---|---|---|---|"]
+    for k in (t, tm):
+        if k:
+            lines.append(f"| `{k['name'][:90]}` | {k['calls']} | {k['avg_us']:.2f} | {k['min_us']:.2f} | "
+                         f"{k['max_us']:.2f} |")
+    lines += ["", f"Algorithmic flops per call (4 d per visible (row, key) pair): {flops:,}.  At the attention "
+                  f"kernel's average duration: {tf:.1f} TFLOP/s = {100 * tf / 2500:.2f} % of the 2.5 PFLOP/s bf16 "
+                  f"MFMA peak; over the whole call ({call_us:.1f} µs): {tf_call:.1f} TFLOP/s = "
+                  f"{100 * tf_call / 2500:.2f} %."]
+    data = {"source_hash": source_hash("prefix"), "trace": trace, "algorithmic_flops": flops,
+            "achieved_TFLOPs": tf, "achieved_TFLOPs_call": tf_call, "key_range_splits": splits,
+            "workspace_bytes": ws, "taken": time.strftime("%Y-%m-%d %H:%M:%S")}
     if counters:
         # unique bytes: every (cached + new) token's K and V once, the queries,
-        # the block-table rows and per-sequence metadata; writes: the output rows
+        # the block-table rows and per-sequence metadata; writes: the output
+        # rows, or the float32 partials when split (read back by the merge)
         eb = 4 if c["dtype"] == "f32" else 2
         rows = sum(c["ql"]) * c["H"] * c["d"] * eb
         tokens = sum(a + b for a, b in zip(c["ctx"], c["ql"]))
         blocks = sum(-(-(a + b) // c["bs"]) for a, b in zip(c["ctx"], c["ql"]))
         alg_r = tokens * c["KVH"] * 2 * c["d"] * eb + rows + 4 * blocks + 3 * 4 * len(c["ql"])
-        f, w = counters["phase1_fetch_bytes"], counters["phase1_write_bytes"]
+        alg_w = ws if splits > 1 else rows
+        f, w = counters["prefix_fetch_bytes"], counters["prefix_write_bytes"]
+        fm, wm = counters["prefix_merge_fetch_bytes"], counters["prefix_merge_write_bytes"]
         data["counters"] = counters
         data["traffic_bytes"] = f + w
-        data["unique_read_bytes"], data["unique_write_bytes"] = alg_r, rows
+        data["merge_traffic_bytes"] = fm + wm
+        data["unique_read_bytes"], data["unique_write_bytes"] = alg_r, alg_w
         lines += ["", "HBM counters (`rocprofv3 --pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, over the same bench "
-                      "command and over `bench.py --mode copy`, a 1 GiB copy; prefix-kernel dispatches only):", "",
+                      "command and over `bench.py --mode copy`, a 1 GiB copy):", "",
                   "| quantity | value |", "|---|---|",
                   f"| scale factors (known / counted) | fetch {counters['FETCH_SIZE_scale']:.4f}, "
                   f"write {counters['WRITE_SIZE_scale']:.4f} |",
-                  f"| FETCH_SIZE / WRITE_SIZE per launch (KiB, raw) | {counters['FETCH_SIZE_phase1_kib']:.1f} / "
-                  f"{counters['WRITE_SIZE_phase1_kib']:.1f} |",
-                  f"| HBM read / write bytes (scaled) | {f:,.0f} / {w:,.0f} |",
-                  f"| unique reads (K/V of every token once, queries, tables) / writes (output) | "
-                  f"{alg_r:,} / {rows:,} |",
-                  f"| measured / unique | reads {f / alg_r:.4f}, writes {w / rows:.4f} |"]
+                  f"| attention kernel: FETCH_SIZE / WRITE_SIZE per launch (KiB, raw) | "
+                  f"{counters['FETCH_SIZE_prefix_kib']:.1f} / {counters['WRITE_SIZE_prefix_kib']:.1f} |",
+                  f"| attention kernel: HBM read / write bytes (scaled) | {f:,.0f} / {w:,.0f} |",
+                  f"| unique reads (K/V of every token once, queries, tables) / writes (output, or the "
+                  f"partials when split) | {alg_r:,} / {alg_w:,} |",
+                  f"| attention kernel: measured / unique | reads {f / alg_r:.4f}, writes {w / alg_w:.4f} |"]
+        if tm:
+            lines.append(f"| merge kernel: HBM read / write bytes (scaled) | {fm:,.0f} / {wm:,.0f} |")
     with open(os.path.join(out, name + ".md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     with open(os.path.join(out, name + ".json"), "w") as fh:

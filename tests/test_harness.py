@@ -43,8 +43,24 @@ def test_v1_summary_uses_single_pass_bytes(tmp_path):
     assert abs(data["phase1_achieved_GBps"] - alg["v1"] / 10e-6 / 1e9) < 1e-6
 
 
+def _prefix_trace(avg_us, merge_us=None):
+    t = {"command": "rocprofv3 ...", "prefix": {"name": "prefix_kernel", "calls": 3, "avg_us": avg_us,
+                                                "min_us": avg_us, "max_us": avg_us}}
+    if merge_us is not None:
+        t["prefix_merge"] = {"name": "prefix_merge_kernel", "calls": 3, "avg_us": merge_us, "min_us": merge_us,
+                             "max_us": merge_us}
+    return t
+
+
+def _prefix_counters(fetch, write, mfetch=0.0, mwrite=0.0):
+    return {"prefix_fetch_bytes": fetch, "prefix_write_bytes": write, "prefix_merge_fetch_bytes": mfetch,
+            "prefix_merge_write_bytes": mwrite, "FETCH_SIZE_copy_kib": 1.0, "WRITE_SIZE_copy_kib": 1.0,
+            "FETCH_SIZE_scale": 2.0, "WRITE_SIZE_scale": 1.0, "FETCH_SIZE_prefix_kib": fetch / 2048,
+            "WRITE_SIZE_prefix_kib": write / 1024}
+
+
 def test_prefix_summary_unique_bytes(tmp_path):
-    H.write_prefix_summary(str(tmp_path), _trace(3000.0), _counters(6.0e8, 2.5e7))
+    H.write_prefix_summary(str(tmp_path), _prefix_trace(3000.0), _prefix_counters(6.0e8, 2.5e7))
     data = json.load(open(tmp_path / "prefix_attention.json"))
     # 4 sequences of 16384 cached + 512 new tokens, kv_h 4, d 256, bf16; 24 query heads
     tokens = 4 * (16384 + 512)
@@ -52,8 +68,26 @@ def test_prefix_summary_unique_bytes(tmp_path):
     rows = 4 * 512 * 24 * 256 * 2
     tables = 4 * (16384 + 512) // 16
     assert data["unique_read_bytes"] == kv + rows + 4 * tables + 3 * 4 * 4
-    assert data["unique_write_bytes"] == rows
+    assert data["unique_write_bytes"] == rows   # unsplit (no bench line in the log): the output rows
     assert data["traffic_bytes"] == 6.0e8 + 2.5e7
+    assert data["key_range_splits"] == 1
+
+
+def test_prefix_summary_split_call(tmp_path):
+    # the bench line in the trace log names the split; the attention kernel then
+    # writes the float32 partials (the workspace), and the call's time adds the merge
+    ws = 2 * 384 * 128 * 258 * 4
+    (tmp_path / "trace_prefix.log").write_text(
+        "progress line\n" + json.dumps({"key_range_splits": 2, "workspace_bytes": ws}) + "\n")
+    H.write_prefix_summary(str(tmp_path), _prefix_trace(1000.0, 25.0),
+                           _prefix_counters(3.1e8, 1.0e8, 1.0e8, 2.5e7))
+    data = json.load(open(tmp_path / "prefix_attention.json"))
+    assert data["key_range_splits"] == 2 and data["unique_write_bytes"] == ws
+    assert data["traffic_bytes"] == 3.1e8 + 1.0e8 and data["merge_traffic_bytes"] == 1.0e8 + 2.5e7
+    flops = bench.prefix_flops(**{k: bench.PREFIX_CASE[k] for k in ("ctx", "ql", "H", "d")})
+    assert abs(data["achieved_TFLOPs_call"] - flops / 1025e-6 / 1e12) < 1e-6
+    text = open(tmp_path / "prefix_attention.md").read()
+    assert "prefix_merge_kernel" in text and "Key ranges per row block: 2" in text
 
 
 def test_bench_reads_traffic_only_for_current_sources():
@@ -78,7 +112,7 @@ def test_source_hash_covers_the_launch_plan(tmp_path, monkeypatch):
     # the planner (schedule, grid, LDS sizing, scale folding) lives in api.hip
     # and the ABI's constants in pav2.h: editing either must invalidate the
     # stored counters, as editing a kernel does
-    for mode in ("decode", "cache_write"):
+    for mode in ("decode", "prefix", "cache_write"):
         names = [os.path.basename(f) for f in H.KERNEL_SOURCES[mode]]
         assert "api.hip" in names and "pav2.h" in names
     assert any(n.startswith("phase1_") for n in map(os.path.basename, H.KERNEL_SOURCES["decode"]))
