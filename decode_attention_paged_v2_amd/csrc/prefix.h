@@ -28,7 +28,9 @@ struct PrefixParams {
     // row block's tiles into that many ranges whose normalised partial
     // outputs (float32) and statistics go to `part`, merged by a second kernel
     int splits = 1;
-    float *part = nullptr;           // [splits * num_work * 128] x (D + 2) floats: o, then m, then l
+    // o: per (range, row block) item [D / 4][128 rows][4] floats, then m and
+    // l: [splits * num_work * 128] floats each
+    float *part = nullptr;
 };
 
 constexpr int kPrefixMfmaRows = 128;   // query rows per workgroup

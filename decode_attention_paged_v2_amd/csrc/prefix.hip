@@ -71,6 +71,14 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
+// Wait until every copy this wavefront issued into LDS has landed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left alone).  A barrier publishes
+// LDS writes, but the compiler treats a copy into LDS as a load whose result
+// only its own wavefront needs and may leave it in flight across the barrier,
+// so every barrier that hands copied tiles to the other wavefronts follows
+// this wait.
+__device__ __forceinline__ void copies_landed() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int DT>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     if constexpr (DT == BF16)
@@ -481,6 +489,7 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
     if (tb < te) {
         __syncthreads();   // the zeroed tiles are in place before any copy lands
         copy_k(tb, blk_v, k0);
+        copies_landed();
         __syncthreads();
         copy_v(tb, blk_v, v0);
         blk_v = key_block(tb + 1);
@@ -508,6 +517,7 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
                 else copy_v_one(q - KPW, T + 1, blk_v, vnxt);
             });
         };
+        copies_landed();
         __syncthreads();
         step(IC<7>{}, vcur, 0, kcur, 0, 2 * T + 1, dma);
         blk_v = blk_k;
@@ -517,6 +527,7 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
     auto last = [&](auto par) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par)::value;
         const uint8_t *vcur = PAR ? vl1 : vl0;
+        copies_landed();
         __syncthreads();
         zero_tail(te - 1, PAR ? v1 : v0);
         __syncthreads();
@@ -541,15 +552,19 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
     const float lr = lsum + __shfl_xor(lsum, 32);   // both half-waves' keys
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
     if (P.splits > 1) {   // a partial over tiles [tb, te): o / l, the offset m and l, in float32
-        const int64_t pi = ((int64_t)(split * P.num_work + wg) * kRows) + wv * 32 + lrow;
-        float *po = P.part + pi * D;
+        // o as [head-dim / 4][row][4] per item: column group c4 = d / 4 = 8 dt +
+        // 2 q + half, so each store instruction writes two 512-byte runs
+        const int64_t item_base = (int64_t)(split * P.num_work + wg) * kRows;
+        const int64_t pi = item_base + wv * 32 + lrow;
+        float *po = P.part + item_base * D + (wv * 32 + lrow) * 4;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int d = 32 * dt + 8 * q + 4 * half;
-                *reinterpret_cast<float4 *>(po + d) = make_float4(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv,
-                                                                  o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
+                const int c4 = 8 * dt + 2 * q + half;
+                *reinterpret_cast<float4 *>(po + c4 * kRows * 4) =
+                    make_float4(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv, o[dt][4 * q + 2] * inv,
+                                o[dt][4 * q + 3] * inv);
             }
         if (half == 0) {
             const int64_t np = (int64_t)P.splits * P.num_work * kRows;
@@ -575,8 +590,8 @@ __global__ void __launch_bounds__(256) prefix_kernel(const PrefixParams P) {
 // online softmax's combination of partial results over disjoint key sets.
 template <int DT, int D>
 __global__ void __launch_bounds__(256) prefix_merge_kernel(const PrefixParams P) {
-    constexpr int RPB = 16;   // rows per workgroup: 16 threads per row, each a float4 column stride 16
-    const int wg = blockIdx.x / (kRows / RPB), rr = (blockIdx.x % (kRows / RPB)) * RPB + (threadIdx.x >> 4);
+    constexpr int RPB = 16;   // rows per workgroup: 16 threads per column group (rows fastest, coalesced)
+    const int wg = blockIdx.x / (kRows / RPB), rr = (blockIdx.x % (kRows / RPB)) * RPB + (threadIdx.x & 15);
     const int RB = P.row_blocks, KVH = P.num_kv_heads, gqa = P.gqa;
     const int s = wg / (KVH * RB), g = (wg / RB) % KVH, rb = wg % RB;
     const int q0 = P.query_start_loc[s];
@@ -603,14 +618,14 @@ __global__ void __launch_bounds__(256) prefix_merge_kernel(const PrefixParams P)
     uint8_t *orow = reinterpret_cast<uint8_t *>(P.out) + ((int64_t)(q0 + jq) * P.num_heads + g * gqa + rq) * D * 2;
 #pragma unroll
     for (int k = 0; k < (D / 4 + 15) / 16; ++k) {
-        const int c4 = (threadIdx.x & 15) + 16 * k;
+        const int c4 = (threadIdx.x >> 4) + 16 * k;
         if (c4 >= D / 4) break;
         float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
 #pragma unroll
         for (int c = 0; c < kPrefixMaxSplits; ++c) {
             if (c < P.splits && wc[c] > 0.0f) {
-                const int64_t pi = (int64_t)(c * P.num_work + wg) * kRows + rr;
-                const float4 v = *reinterpret_cast<const float4 *>(P.part + pi * D + 4 * c4);
+                const int64_t ib = (int64_t)(c * P.num_work + wg) * kRows;
+                const float4 v = *reinterpret_cast<const float4 *>(P.part + ib * D + ((int64_t)c4 * kRows + rr) * 4);
                 a0 = fmaf(wc[c], v.x, a0);
                 a1 = fmaf(wc[c], v.y, a1);
                 a2 = fmaf(wc[c], v.z, a2);

@@ -189,6 +189,20 @@ def test_prefix_full_size_sampled():
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     got = out.cpu()
+    # every output, not only the sampled rows: a second call is bit-identical
+    # (the tiles' hand-off between wavefronts leaves nothing to timing), and
+    # the unsplit call agrees to the output dtype's rounding
+    again = torch.full_like(pw.query, float("nan"))
+    whole = torch.full_like(pw.query, float("nan"))
+    pav2.paged_prefix_attention(again, pw.query, pw.key_cache, pw.value_cache, pw.block_tables, pw.query_start_loc,
+                                pw.context_lens, max(c["ql"]), max_seq)
+    pav2.paged_prefix_attention(whole, pw.query, pw.key_cache, pw.value_cache, pw.block_tables, pw.query_start_loc,
+                                pw.context_lens, max(c["ql"]), max_seq, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(again.cpu().view(torch.int16), got.view(torch.int16))
+    wd = whole.cpu().double()
+    diff = (wd - got.double()).abs().max().item()
+    assert diff <= 2 * _tol.ulp(wd.abs().max().item(), torch.bfloat16), diff
     kb, vb = oracle.reshape_and_cache(host.key, host.value, host.key_cache, host.value_cache, host.slot_mapping,
                                       block_size=c["bs"], cache_dtype=oracle.BF16)
     kc = torch.from_numpy(kb).view(torch.bfloat16).reshape(host.key_cache.shape)
