@@ -508,9 +508,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="long_gqa", choices=list(W.SPECS))
-    ap.add_argument("--entry", default="v2", choices=["v2", "v1", "auto"],
-                    help="v2: both phases (the default); v1: the single-pass entry point; "
-                         "auto: the planner's choice")
+    ap.add_argument("--entry", default="auto", choices=["v2", "v1", "auto"],
+                    help="auto (the default): the library's V1 / V2 dispatch (forward_decode's plan); "
+                         "v2: both phases; v1: the single-pass entry point")
     ap.add_argument("--single", action="store_true",
                     help="measure the --config workload alone (no configs map, block-sparse line or "
                          "read-stream figure, no oracle check)")

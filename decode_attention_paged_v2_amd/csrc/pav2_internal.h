@@ -142,13 +142,18 @@ inline bool phase1_compact(int num_seqs) {
 
 // Dispatch between the single-pass kernel and the two-phase path: single
 // pass when every sequence fits one partition (no combine needed), or when the
-// (sequence, kv head, head group) workgroups alone fill the chip several
-// times over and the sequences are short enough that walking their
-// partitions in one workgroup does not leave a long tail.  Planned for the
-// MI355X's 256 compute units, without querying the device.
+// (sequence, kv head, head group) workgroups alone give every compute unit
+// two or more and no sequence spans more than 32 partitions (a workgroup then
+// streams up to 16K tokens without the per-partition outputs, the second
+// launch and its gap; for equal lengths it is the faster path, e.g. 64 x 16K
+// tokens with an e4m3 cache: 0.325 ms single pass against 0.399 ms for the
+// two phases).  Decided from the shapes alone (no read of seq_lens), as the
+// pages' own rule is; a batch that puts one long sequence among many short
+// ones walks that sequence's partitions serially.  Planned for the MI355X's
+// 256 compute units, without querying the device.
 constexpr int kPlanCUs = 256;
-constexpr int kSinglePassMinRounds = 4;     // workgroups >= this many per CU
-constexpr int kSinglePassMaxPartitions = 8; // and at most this many partitions per sequence
+constexpr int kSinglePassMinRounds = 2;      // workgroups >= this many per CU
+constexpr int kSinglePassMaxPartitions = 32; // and at most this many partitions per sequence
 inline bool prefer_single_pass(int64_t seq_items, int max_num_partitions) {
     if (max_num_partitions <= 1) return true;
     return seq_items >= (int64_t)kSinglePassMinRounds * kPlanCUs &&

@@ -106,7 +106,7 @@ def _bench_args(config: str, mode: str, steps: int, warmup: int, entry: str = "v
     args = args + ["--single"]
     if mode == "blocksparse":
         return args + ["--mode", "blocksparse"]
-    return args + (["--entry", "v1"] if entry == "v1" else [])
+    return args + ["--entry", "v1" if entry == "v1" else "v2"]   # (the bench's default is the planner's choice)
 
 
 def _tag(mode: str, config: str, entry: str) -> str:

@@ -180,7 +180,8 @@ def test_plan(cfg, expect):
         assert p[k] == v, (k, p)
     assert p["phase1_threads"] == 256 and p["phase2_threads"] in (256, 1024)
     assert p["phase1_compact"] == (1 if cfg["num_seqs"] > 1 else 0)
-    assert p["use_v1"] == 0
+    items = cfg["num_seqs"] * cfg["num_kv_heads"] * p["head_groups"]
+    assert p["use_v1"] == (1 if items >= 2 * 256 and cfg["max_num_partitions"] <= 32 else 0)
     assert p["v1_workgroups"] == cfg["num_seqs"] * cfg["num_kv_heads"] * p["head_groups"]
     assert p["v1_lds_bytes"] <= p["phase1_lds_bytes"]
     assert 0 < p["phase1_lds_bytes"] <= 160 * 1024
@@ -191,15 +192,16 @@ def test_plan(cfg, expect):
     (1, 4, 1, 1),       # one partition: no combine needed
     (4, 4, 1, 1),
     (256, 8, 4, 1),     # 2048 (seq, kv head) workgroups, 4 partitions each
-    (128, 8, 8, 1),     # 1024 workgroups = 4 per compute unit
-    (127, 8, 8, 0),     # just under 4 per compute unit
-    (256, 8, 9, 0),     # more than 8 partitions per sequence
+    (64, 8, 32, 1),     # 512 workgroups = 2 per compute unit, 32 partitions (16K tokens)
+    (63, 8, 32, 0),     # just under 2 per compute unit
+    (64, 8, 33, 0),     # more than 32 partitions per sequence
+    (32, 8, 8, 0),      # 256 workgroups: one per compute unit
     (4, 4, 196, 0),     # long context
 ])
 def test_plan_v1_choice(num_seqs, num_kv_heads, maxp, expect):
     """Single pass when every sequence fits one partition, or when the (seq, kv
-    head, head group) workgroups fill the 256 compute units 4 times over and
-    sequences span at most 8 partitions."""
+    head, head group) workgroups give the 256 compute units two or more each
+    and sequences span at most 32 partitions."""
     p = pav2.plan(num_seqs, 8 * num_kv_heads, num_kv_heads, 128, 16, maxp, B.BF16, B.BF16)
     assert p["use_v1"] == expect
 

@@ -23,7 +23,8 @@ def _counters(fetch, write):
 def test_bench_args_select_entry_and_mode():
     a = H._bench_args("fp8_kv", "decode", 3, 1, "v1")
     assert a[a.index("--entry") + 1] == "v1" and "--mode" not in a
-    assert "--entry" not in H._bench_args("fp8_kv", "decode", 3, 1)
+    a2 = H._bench_args("fp8_kv", "decode", 3, 1)   # both phases even where the planner would take V1
+    assert a2[a2.index("--entry") + 1] == "v2"
     p = H._bench_args("long_gqa", "prefix", 3, 1)
     assert p[p.index("--mode") + 1] == "prefix"
     assert H._tag("decode", "tiny", "v1") == "decode_v1_tiny" and H._tag("prefix", "tiny", "v2") == "prefix"
