@@ -197,7 +197,7 @@ def sq(config: str, out: str) -> dict:
         d = os.path.join(out, f"sq{i}_{config}")
         shutil.rmtree(d, ignore_errors=True)
         bench = [sys.executable, BENCH, "--config", config, "--steps", "3", "--warmup", "1",
-                 "--no-cpu-baseline", "--single"]
+                 "--no-cpu-baseline", "--single", "--entry", "v2"]
         cmd = ["rocprofv3", "--pmc", *counters, "-d", d, "-o", "run", "--output-format", "csv", "--"] + bench
         _run(cmd, os.path.join(out, f"sq{i}_{config}.log"), 120)
         per = {}
