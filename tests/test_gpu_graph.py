@@ -92,3 +92,42 @@ def test_graph_prefix():
     run()
     torch.cuda.synchronize()
     replay_and_check(run, [out], [out.clone()])
+
+
+def test_graph_prefix_split_with_workspace():
+    """Few row blocks over a long context: the captured call is the split one
+    (attention kernel, then the merge) over a workspace allocated beforehand."""
+    ctx, ql = [3000], [40]
+    pw = W.prefix_workload(ctx, ql, 8, 1, 128, 16, dtype="bf16", seed=11, device=DEV)
+    pav2.reshape_and_cache(pw.key, pw.value, pw.key_cache, pw.value_cache, pw.slot_mapping)
+    need = pav2.prefix_workspace_bytes(pw.query, pw.key_cache, pw.value_cache, pw.context_lens, 40, 3040)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(pw.query)
+
+    def run():
+        pav2.paged_prefix_attention(out, pw.query, pw.key_cache, pw.value_cache, pw.block_tables,
+                                    pw.query_start_loc, pw.context_lens, 40, 3040, workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    replay_and_check(run, [out], [out.clone()])
+
+
+def test_graph_decode_blocksparse():
+    wl = W.generate(W.SMALL_SPECS["ragged_alibi"]).to(DEV)
+    S, H, D, P = wl.num_seqs, wl.num_heads, wl.head_size, wl.max_num_partitions
+    out = torch.empty_like(wl.query)
+    es = torch.zeros((S, H, P), dtype=torch.float32, device=DEV)
+    ml = torch.zeros_like(es)
+    tmp = torch.zeros((S, H, P, D), dtype=wl.q_dtype, device=DEV)
+
+    def run():
+        pav2.paged_attention_v2_blocksparse(out, es, ml, tmp, wl.query, wl.key_cache, wl.value_cache,
+                                            wl.num_kv_heads, wl.scale, wl.block_tables, wl.seq_lens,
+                                            wl.block_size, wl.max_seq_len, wl.alibi_slopes, "auto",
+                                            wl.k_scale, wl.v_scale, tp_rank=0, blocksparse_local_blocks=2,
+                                            blocksparse_vert_stride=3, blocksparse_block_size=32,
+                                            blocksparse_head_sliding_step=1)
+    run()
+    torch.cuda.synchronize()
+    replay_and_check(run, [out, es, ml], [out.clone(), es.clone(), ml.clone()])
