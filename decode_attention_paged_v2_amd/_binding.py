@@ -29,7 +29,8 @@ class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "phase1_workgroups", "phase1_threads", "phase1_lds_bytes", "head_groups",
         "waves_per_partition", "phase2_workgroups", "phase2_threads", "phase2_lds_bytes",
-        "phase1_compact", "use_v1", "v1_workgroups", "v1_lds_bytes")]
+        "phase1_compact", "use_v1", "v1_workgroups", "v1_lds_bytes", "phase1_rounds",
+        "phase1_xcd_classes")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -126,6 +126,8 @@ void make_plan(const Shape &s, pav2_plan_t *pl) {
     pl->phase1_lds_bytes =
         pav2::phase1_lds_bytes(gqa, s.head_size, pav2::kPhase1Waves, bs_log2, s.num_seqs, compact);
     pl->phase1_compact = compact ? 1 : 0;
+    pl->phase1_rounds = compact ? pav2::phase1_compact_rounds(s.num_seqs) : 0;
+    pl->phase1_xcd_classes = compact && pav2::phase1_xcd_classes(s.num_seqs, s.num_kv_heads, hg) ? 1 : 0;
     pl->phase2_workgroups = pav2::phase2_workgroups((int64_t)s.num_seqs * s.num_heads, s.max_num_partitions);
     {
         const int wpp = pav2::phase2_waves_per_pair(s.max_num_partitions);
@@ -203,6 +205,8 @@ int run_phase1(float *exp_sums, float *max_logits, void *tmp_output, const void 
     p.max_num_partitions = sh.max_num_partitions;
     p.num_work = sh.num_seqs * sh.num_kv_heads * pl.head_groups * sh.max_num_partitions;
     p.sched = pl.phase1_compact;
+    p.compact_rounds = pl.phase1_rounds > 0 ? pl.phase1_rounds : pav2::kPhase1CompactRounds;
+    p.xcd_classes = pl.phase1_xcd_classes;
     p.head_stride = (int64_t)sh.head_size * sh.block_size * elem_bytes(sh.kvdt);
     p.blk_stride = p.head_stride * sh.num_kv_heads;
     p.scale_log2 = scale * k_scale * 1.4426950408889634f;

@@ -184,6 +184,9 @@ phase1_kernel(const Phase1Params P) {
     const int maxP = P.max_num_partitions;
     const int HG = P.head_groups;
     const int KVH = P.num_kv_heads;
+    // compact schedule by (kv head, head group) class per XCD (host-checked:
+    // KVH * HG is a multiple of 8; the grid, a multiple of 8, is re-checked)
+    const bool classes = COMPACT && P.xcd_classes != 0 && (gridDim.x & 7) == 0;
     // (prefix attention merges nothing across wavefronts: no partial-output area)
     const int heads_alloc = PREFIX ? 0 : min(P.gqa, kMaxHeadsPerGroup);
     constexpr int kBsLog2 = BS == 16 ? 4 : (BS == 32 ? 5 : -1);
@@ -276,13 +279,24 @@ phase1_kernel(const Phase1Params P) {
         if (tid == 0) s_pref[P.num_seqs] = total;
         total = __builtin_amdgcn_readfirstlane(total);   // wave-uniform: keep the item loop scalar
         __syncthreads();
-        const int64_t n_items = (int64_t)total * KVH * HG;
-        // balanced contiguous ranges; the XCD-blocked numbering is a
-        // permutation of the workgroups when the grid is a multiple of 8
-        const bool xcd = kPhase1XcdRanges && (gridDim.x & 7) == 0;
-        const int b = xcd ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
-        item = (int)(n_items * b / gridDim.x);
-        item_end = (int)(n_items * (b + 1) / gridDim.x);
+        if (classes) {
+            // XCD x = blockIdx % 8 walks whole (kv head, head group) classes
+            // x * C/8 .. (x + 1) * C/8 - 1; items are numbered class-major
+            // (class * total + the (sequence, partition) index), and the XCD's
+            // workgroups take balanced contiguous ranges of its list
+            const int64_t len = (int64_t)total * ((KVH * HG) >> 3);
+            const int x = blockIdx.x & 7, bw = blockIdx.x >> 3, nw = gridDim.x >> 3;
+            item = (int)(len * x + len * bw / nw);
+            item_end = (int)(len * x + len * (bw + 1) / nw);
+        } else {
+            const int64_t n_items = (int64_t)total * KVH * HG;
+            // balanced contiguous ranges; the XCD-blocked numbering is a
+            // permutation of the workgroups when the grid is a multiple of 8
+            const bool xcd = kPhase1XcdRanges && (gridDim.x & 7) == 0;
+            const int b = xcd ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
+            item = (int)(n_items * b / gridDim.x);
+            item_end = (int)(n_items * (b + 1) / gridDim.x);
+        }
     } else {
         const int nblk = gridDim.x;
         item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
@@ -323,9 +337,18 @@ phase1_kernel(const Phase1Params P) {
         s = wg / (HG * KVH);
         p = PREFIX ? item / (kPartition / kPrefixSlice) : item;
     } else if constexpr (COMPACT) {
-        int r = item / HG;
-        g = r % KVH;
-        r /= KVH;
+        int r;
+        if (classes) {
+            const int total = __builtin_amdgcn_readfirstlane(s_pref[P.num_seqs]);
+            const int c = item / total;
+            r = item - c * total;
+            hg = c % HG;
+            g = c / HG;
+        } else {
+            r = item / HG;
+            g = r % KVH;
+            r /= KVH;
+        }
         int lo = 0, hi = P.num_seqs;   // last sequence with prefix <= r (scalar search)
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -1086,7 +1109,7 @@ hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
     if (SCHED == 1) {
         // at most kPhase1CompactRounds resident rounds of workgroups, each
         // walking a balanced range of the used items
-        const int cap = kPhase1CompactRounds * device_cu_count(dev) * resident_per_cu(state, fn, dev, WAVES * 64, lds);
+        const int cap = p.compact_rounds * device_cu_count(dev) * resident_per_cu(state, fn, dev, WAVES * 64, lds);
         grid = grid < cap ? grid : cap;
     } else if (SCHED == 2) {
         grid = p.num_work;   // one workgroup per (sequence, kv head, head group)

@@ -277,12 +277,18 @@ typedef struct {
     int phase2_threads;
     int phase2_lds_bytes;
     int phase1_compact;       /* 1: phase 1 walks a compact list of used partitions
-                                 (grid: min(phase1_workgroups, 8 resident rounds)) */
+                                 (grid: min(phase1_workgroups, phase1_rounds
+                                 resident rounds)) */
     int use_v1;               /* 1: the single-pass entry point is the faster choice
                                  (every sequence in one partition, or enough
                                  (sequence, kv head) work to fill the chip) */
     int v1_workgroups;        /* single-pass grid: num_seqs * num_kv_heads * head_groups */
     int v1_lds_bytes;         /* dynamic LDS per single-pass workgroup */
+    int phase1_rounds;        /* compact schedule: resident rounds of workgroups
+                                 (1 from 16 sequences on, else 8; 0 when dense) */
+    int phase1_xcd_classes;   /* compact schedule: 1 when each XCD takes whole
+                                 (kv head, head group) classes (16 or more
+                                 sequences, classes a multiple of 8) */
 } pav2_plan_t;
 
 int pav2_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size,

@@ -186,6 +186,26 @@ def test_plan(cfg, expect):
     assert p["v1_lds_bytes"] <= p["phase1_lds_bytes"]
     assert 0 < p["phase1_lds_bytes"] <= 160 * 1024
     assert p["phase2_lds_bytes"] == 0
+    compact = cfg["num_seqs"] > 1
+    assert p["phase1_rounds"] == ((1 if cfg["num_seqs"] >= 16 else 8) if compact else 0)
+    assert p["phase1_xcd_classes"] == (1 if compact and cfg["num_seqs"] >= 16 and
+                                       (cfg["num_kv_heads"] * p["head_groups"]) % 8 == 0 else 0)
+
+
+@pytest.mark.parametrize("num_seqs,num_kv_heads,gqa,rounds,classes", [
+    (4, 4, 6, 8, 0),      # a few long sequences: 8 resident rounds, items in order
+    (15, 8, 4, 8, 0),     # just under the many-sequence bound
+    (16, 8, 4, 1, 1),     # many sequences, 8 (kv head, group) classes: one per XCD
+    (256, 8, 4, 1, 1),
+    (32, 4, 4, 1, 0),     # 4 classes: one round, items in order
+    (32, 4, 20, 1, 1),    # 4 kv heads x 2 head groups = 8 classes
+    (32, 16, 2, 1, 1),    # 16 classes: two per XCD
+    (32, 12, 2, 1, 0),    # 12 classes
+])
+def test_plan_compact_rounds_and_classes(num_seqs, num_kv_heads, gqa, rounds, classes):
+    p = pav2.plan(num_seqs=num_seqs, num_heads=num_kv_heads * gqa, num_kv_heads=num_kv_heads, head_size=128,
+                  block_size=16, max_num_partitions=8, query_dtype=B.F16, kv_cache_dtype=B.F16)
+    assert (p["phase1_rounds"], p["phase1_xcd_classes"]) == (rounds, classes)
 
 
 @pytest.mark.parametrize("num_seqs,num_kv_heads,maxp,expect", [

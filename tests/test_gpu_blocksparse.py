@@ -124,6 +124,17 @@ def test_blocksparse_single_sequence_dense_schedule(sp):
     compare(wl, run_gpu(wl, sp), run_oracle(wl, sp))
 
 
+@pytest.mark.parametrize("H,KVH", [(32, 8), (32, 16)])
+def test_blocksparse_many_sequences_compact_classes(H, KVH):
+    """20 sequences: one resident round of workgroups, each XCD walking whole
+    (kv head, head group) classes (8 and 16 classes)."""
+    sp = (1, 2, 3, 32, 1)
+    wl = make(LENS + [700, 90, 1536, 0, 33, 2000, 511, 4, 1025, 260, 1700, 3000], H=H, KVH=KVH, D=64, q="f16",
+              kv="f16", alibi=True, seed=H + KVH)
+    assert wl.num_seqs == 20
+    compare(wl, run_gpu(wl, sp), run_oracle(wl, sp))
+
+
 def test_blocksparse_many_heads_per_group():
     """gqa = 20: two 16-head groups per kv head, heads with different stripes in each."""
     sp = (0, 1, 7, 32, 3)

@@ -20,6 +20,7 @@ import torch
 import oracle
 import _tol
 import decode_attention_paged_v2_amd as pav2
+from decode_attention_paged_v2_amd import _binding as B
 from decode_attention_paged_v2_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -273,6 +274,32 @@ def test_edge_dtypes_head_sizes(q, kv, D):
     ks, vs = (0.05, 0.04) if kv == "fp8_e4m3" else (1.0, 1.0)
     spec = W.Spec(f"edge_{q}_{kv}_{D}", 6, 2, D, 16, q, kv, lambda g: EDGE_LENS,
                   pool=lambda n: n + 9, alibi=(D % 32 == 16), k_scale=ks, v_scale=vs, seed=D)
+    wl = W.generate(spec, poison=True)
+    g = run_gpu(wl.to(DEV))
+    compare(wl, g, run_oracle(wl))
+
+
+CLASS_LENS = [0, 1, 700, 513, 2049, 31, 512, 1536, 0, 90, 1100, 3000, 17, 1025, 64, 2000, 511, 4, 1700, 260]
+
+
+@pytest.mark.parametrize("H,KVH,q,kv", [
+    (32, 8, "f16", "f16"),           # 8 (kv head, group) classes: one per XCD
+    (32, 16, "bf16", "bf16"),        # 16 classes: two per XCD
+    (80, 4, "f16", "f16"),           # 4 kv heads x 2 head groups of 20 query heads
+    (64, 8, "bf16", "fp8_e4m3"),
+    (24, 12, "f16", "f16"),          # 12 classes: one round, items in order
+])
+def test_many_sequences_compact_classes(H, KVH, q, kv):
+    """20 ragged sequences (empty ones included): the compact grid is one
+    resident round and, where the classes are a multiple of 8, each XCD walks
+    whole (kv head, head group) classes."""
+    plan = pav2.plan(num_seqs=len(CLASS_LENS), num_heads=H, num_kv_heads=KVH, head_size=64, block_size=16,
+                     max_num_partitions=6, query_dtype=B.F16, kv_cache_dtype=B.F16)
+    assert plan["phase1_rounds"] == 1
+    assert plan["phase1_xcd_classes"] == (1 if (KVH * plan["head_groups"]) % 8 == 0 else 0)
+    ks, vs = (0.05, 0.04) if kv == "fp8_e4m3" else (1.0, 1.0)
+    spec = W.Spec(f"classes_{H}_{KVH}", H, KVH, 64, 16, q, kv, lambda g: CLASS_LENS, pool=lambda n: n + 5,
+                  alibi=True, k_scale=ks, v_scale=vs, seed=H + KVH)
     wl = W.generate(spec, poison=True)
     g = run_gpu(wl.to(DEV))
     compare(wl, g, run_oracle(wl))
