@@ -497,7 +497,13 @@ phase1_kernel(const Phase1Params P) {
     constexpr int UPW = PREFIX ? kPrefixSlice / UNIT : (kPartition / UNIT) / WAVES;   // units per wavefront
     const int nunits = (n_tok + UNIT - 1) / UNIT;
     // Block-sparse: the wavefronts deal out the list of attended units
-    // (ascending) round-robin; entries past the list's end are -1.
+    // (ascending) round-robin; entries past the list's end are -1.  Such an
+    // entry still runs the unit's loads and matrix work, but every lane loads
+    // the same few lines at the start of the pool (an address select, one
+    // line per load instruction), its scores are -inf and its V words
+    // zeroed.  Loads thus never depend on a unit's validity: a per-unit
+    // condition there costs the kernel about 120 VGPRs, i.e. its second
+    // wavefront per SIMD.
     int sp_unit[SPARSE ? UPW : 1];
     if constexpr (SPARSE) {
         uint32_t um = 0;
@@ -513,7 +519,7 @@ phase1_kernel(const Phase1Params P) {
     }
     auto unit_of = [&](int u) {
         if constexpr (PREFIX) return (item % (kPartition / kPrefixSlice)) * UPW + u;
-        else if constexpr (SPARSE) return sp_unit[u];
+        else if constexpr (SPARSE) return sp_unit[u] >= 0 ? sp_unit[u] : 0;
         else return wv + WAVES * u;
     };
     auto uvalid = [&](int u) {
@@ -548,6 +554,7 @@ phase1_kernel(const Phase1Params P) {
             const int64_t b = s_bt[o >> bs_log2];
             base = kc + b * blk_stride + (o & bs_mask) * 16 + (grp << (bs_log2 + 4));
         }
+        if constexpr (SPARSE) base = uvalid(u) ? base : kc;
 #pragma unroll
         for (int w = 0; w < NKL; ++w) {
             u32x4 v = {0, 0, 0, 0};
@@ -567,6 +574,7 @@ phase1_kernel(const Phase1Params P) {
             for (int e = 0; e < 8; ++e) {
                 const int tok = o + e;
                 tb[e] = vc + (int64_t)s_bt[tok >> bs_log2] * blk_stride + ((tok & bs_mask) + (col << bs_log2)) * KVB;
+                if constexpr (SPARSE) tb[e] = uvalid(u) ? tb[e] : vc;
             }
 #pragma unroll
             for (int i = 0; i < DPG; ++i) {
@@ -603,6 +611,7 @@ phase1_kernel(const Phase1Params P) {
             const int64_t b = s_bt[o >> bs_log2];
             base = vc + b * blk_stride + (o & bs_mask) * KVB + (col << bs_log2) * KVB;
         }
+        if constexpr (SPARSE) base = uvalid(u) ? base : vc;
 #pragma unroll
         for (int i = 0; i < DPG; ++i) {
             const int dt = part * DPG + i;
@@ -675,12 +684,10 @@ phase1_kernel(const Phase1Params P) {
 
     auto issue = [&](int j) {
         if (j < GK) {
-            if (uvalid(j / KG)) {
 #pragma unroll
-                for (int hh = 0; hh < KH; ++hh) load_k(kbuf[j % PF][hh], j / KG, (j % KG) * KH + hh);
-            }
+            for (int hh = 0; hh < KH; ++hh) load_k(kbuf[j % PF][hh], j / KG, (j % KG) * KH + hh);
         } else if (j < NG) {
-            if (uvalid((j - GK) / VSPLIT)) load_v(vbuf[j % PF], (j - GK) / VSPLIT, (j - GK) % VSPLIT);
+            load_v(vbuf[j % PF], (j - GK) / VSPLIT, (j - GK) % VSPLIT);
         }
     };
 
@@ -694,7 +701,7 @@ phase1_kernel(const Phase1Params P) {
         const int u = j / KG;
         f32x4 acc[KH];
 #pragma unroll
-        for (int hh = 0; hh < KH; ++hh) acc[hh] = uvalid(u) ? qk_tile(kbuf[j % PF][hh]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int hh = 0; hh < KH; ++hh) acc[hh] = qk_tile(kbuf[j % PF][hh]);
         issue(j + PF);
 #pragma unroll
         for (int hh = 0; hh < KH; ++hh) {
@@ -795,10 +802,6 @@ phase1_kernel(const Phase1Params P) {
     for (int j = GK; j < NG; ++j) {
         const int u = (j - GK) / VSPLIT;
         const int part = (j - GK) % VSPLIT;
-        if (!uvalid(u)) {   // block-sparse: nothing loaded, no weight
-            issue(j + PF);
-            continue;
-        }
         if (part == 0) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -818,9 +821,11 @@ phase1_kernel(const Phase1Params P) {
                 osum = mfma_k32<QDT>(ones, pl, osum);
             }
             const int tu = start + unit_of(u) * UNIT;
-            vpartial = tu + UNIT > L;
+            bool unattended = false;   // block-sparse: an entry past the attended list: V words zeroed
+            if constexpr (SPARSE) unattended = !uvalid(u);
+            vpartial = unattended || tu + UNIT > L;
             if (vpartial) {
-                const int nv = L - (tu + 8 * grp);
+                const int nv = unattended ? 0 : L - (tu + 8 * grp);
 #pragma unroll
                 for (int w = 0; w < VW; ++w) {
                     const int nb = min(max(nv - w * TPW, 0), TPW) * KVB;   // valid bytes of the word
