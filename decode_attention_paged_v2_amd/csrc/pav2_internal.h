@@ -189,7 +189,7 @@ inline int phase1_lds_bytes(int gqa, int head_size, int waves, int bs_log2, int 
     int table = (kPartition >> bs_log2) * 4;
     return waves * heads * (d16 + 4) * 4      // per-wave partial outputs
            + 3 * waves * kMaxHeadsPerGroup * 4 // per-wave max and sums
-           + table                             // the partition's block-table slice
+           + table * (sparse ? waves : 1)      // the partition's block-table slice (block-sparse: one per wavefront)
            + (num_seqs + 1 + waves) * 4 * (compact ? 1 : 0)   // partition-count prefix
            + (sparse ? (kMaxHeadsPerGroup + waves) * 4 : 0);   // heads' stripe residues, unit masks
 }

@@ -162,9 +162,16 @@ __device__ __forceinline__ T load_stream(const uint8_t *p) {
 // schedules only): units of a partition that no head of the group attends
 // are never loaded, and scores of tokens a head does not attend are masked.
 template <int QDT, int KVDT, int D, int WAVES, int SCHED, int BS, bool SPARSE>
-__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(kPhase1Occupancy)))
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SCHED == 4 ? 2 : kPhase1Occupancy)))
 phase1_kernel(const Phase1Params P) {
-    constexpr bool COMPACT = SCHED == 1;
+    // Block-sparse wavefront items: the compact list of used partitions, but
+    // each wavefront takes whole items of the workgroup's range by itself
+    // (its own table slice, attended units and running softmax, its own
+    // outputs; no barrier in the item loop), so that items which attend few
+    // units keep four times as many of their latency chains in flight.
+    constexpr bool WAVEIT = SCHED == 4;
+    static_assert(!WAVEIT || SPARSE, "wavefront items: the block-sparse kernels only");
+    constexpr bool COMPACT = SCHED == 1 || WAVEIT;
     // Paged prefix attention: the 16 columns of a group are (query token,
     // head) rows of one chunk, each with its own causal limit, walked like
     // the single pass over the partitions of the sequence.
@@ -199,7 +206,7 @@ phase1_kernel(const Phase1Params P) {
     float *s_l = s_m + WAVES * kMaxHeadsPerGroup;
     float *s_lr = s_l + WAVES * kMaxHeadsPerGroup;
     int *s_bt = reinterpret_cast<int *>(s_lr + WAVES * kMaxHeadsPerGroup);
-    int *s_pref = s_bt + (kPartition >> bs_log2);       // [num_seqs + 1]
+    int *s_pref = s_bt + (WAVEIT ? WAVES : 1) * (kPartition >> bs_log2);   // [num_seqs + 1]
     int *s_wsum = s_pref + P.num_seqs + 1;              // [WAVES]
     // block-sparse: each wavefront's bits of the attended-unit mask
     uint32_t *s_umask = reinterpret_cast<uint32_t *>(COMPACT ? s_wsum + WAVES : s_pref);   // [WAVES]
@@ -328,7 +335,8 @@ phase1_kernel(const Phase1Params P) {
         for (int e = 0; e < VEC; ++e) run_o[k][e] = 0.0f;
     }
 
-    for (; item < item_end; ++item) {
+    if constexpr (WAVEIT) item += __builtin_amdgcn_readfirstlane(tid0 >> 6);   // wavefront w: items w, w + 4, ...
+    for (; item < item_end; item += WAVEIT ? WAVES : 1) {
     int hg = item % HG;
     int s, g, p;
     if constexpr (SINGLE) {
@@ -364,7 +372,7 @@ phase1_kernel(const Phase1Params P) {
         s = w % P.num_seqs;
         p = w / P.num_seqs;
     }
-    if constexpr (COMPACT || SINGLE) __syncthreads();   // the previous item's LDS is free
+    if constexpr ((COMPACT && !WAVEIT) || SINGLE) __syncthreads();   // the previous item's LDS is free
 
     // Lane indices.  In the item loop they are taken from an opaque per-item
     // copy of the thread id, so that lane-derived address terms are recomputed
@@ -384,8 +392,9 @@ phase1_kernel(const Phase1Params P) {
                           : min(kMaxHeadsPerGroup, P.gqa - hg * kMaxHeadsPerGroup);
 
     if (start >= L) {   // unused partition slot (dense and compact schedules)
-        if (!SINGLE && tid < nh) {
-            const int64_t i = ((int64_t)s * P.num_heads + h0 + tid) * maxP + p;
+        const int hi = WAVEIT ? lane : tid;
+        if (!SINGLE && hi < nh) {
+            const int64_t i = ((int64_t)s * P.num_heads + h0 + hi) * maxP + p;
             P.max_logits[i] = -INFINITY;
             P.exp_sums[i] = 0.0f;
         }
@@ -395,11 +404,17 @@ phase1_kernel(const Phase1Params P) {
     const int n_tok = min(kPartition, L - start);
     const int last = start + n_tok - 1;   // ALiBi reference position: the partition's last token
 
+    // the partition's block-table slice (wavefront items: each wavefront's own)
+    int *const s_btw = WAVEIT ? s_bt + wv * (kPartition >> bs_log2) : s_bt;
     {
         const int n_all = kPartition >> bs_log2;
         const int n_used = (n_tok + bs_mask) >> bs_log2;
         const int32_t *bt = P.block_tables + (int64_t)s * P.max_blocks_per_seq + (start >> bs_log2);
-        for (int i = tid; i < n_all; i += WAVES * 64) s_bt[i] = i < n_used ? bt[i] : 0;
+        if constexpr (WAVEIT) {
+            for (int i = lane; i < n_all; i += 64) s_btw[i] = i < n_used ? bt[i] : 0;
+        } else {
+            for (int i = tid; i < n_all; i += WAVES * 64) s_bt[i] = i < n_used ? bt[i] : 0;
+        }
     }
 
     // Query operand (B of S^T = K Q^T): head h0 + col, head-dim slice of K vector
@@ -419,20 +434,23 @@ phase1_kernel(const Phase1Params P) {
     // the block's smallest column limit (its first row's): units below it need no mask
     const int lmin = PREFIX ? (nh > 0 ? pf_ctx + rb0 / P.gqa + 1 : L) : L;
     Words<X * QB / 4> qw[NKL];
+    auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < NKL; ++u) {
-        const int c = 4 * u + grp;
-        const bool ok = hvalid && c < S::kChunks;
+        for (int u = 0; u < NKL; ++u) {
+            const int c = 4 * u + grp;
+            const bool ok = hvalid && c < S::kChunks;
 #pragma unroll
-        for (int k = 0; k < X * QB / 16; ++k) {
-            u32x4 v = {0, 0, 0, 0};
-            if (ok) v = *reinterpret_cast<const u32x4 *>(qrow + (int64_t)c * X * QB + 16 * k);
-            qw[u].w[4 * k + 0] = v[0];
-            qw[u].w[4 * k + 1] = v[1];
-            qw[u].w[4 * k + 2] = v[2];
-            qw[u].w[4 * k + 3] = v[3];
+            for (int k = 0; k < X * QB / 16; ++k) {
+                u32x4 v = {0, 0, 0, 0};
+                if (ok) v = *reinterpret_cast<const u32x4 *>(qrow + (int64_t)c * X * QB + 16 * k);
+                qw[u].w[4 * k + 0] = v[0];
+                qw[u].w[4 * k + 1] = v[1];
+                qw[u].w[4 * k + 2] = v[2];
+                qw[u].w[4 * k + 3] = v[3];
+            }
         }
-    }
+    };
+    if constexpr (!WAVEIT) load_q();   // wavefront items load it per chunk
 
     // ALiBi slope in log2 units (0 without ALiBi, so the bias terms vanish).
     float slope2 = 0.0f;
@@ -441,10 +459,12 @@ phase1_kernel(const Phase1Params P) {
 
     // Block-sparse: sparse blocks above sp_klo are the local window; this
     // lane's head attends the stripe residue sp_res (mod vert_stride).  Each
-    // thread tests kPartition / (WAVES * 64) consecutive tokens against every
-    // head of the group, and a ballot gives each wavefront's 32-token units
-    // their "attended by some head" bits.
+    // thread tests kPartition / (MW * 64) consecutive tokens against every
+    // head of the group (MW: the wavefronts sharing the partition), and a
+    // ballot gives each wavefront's 32-token units their "attended by some
+    // head" bits (wavefront items: all 16 units' bits, in sp_um).
     int sp_res = -1, sp_klo = 0;
+    uint32_t sp_um = 0;
     if constexpr (SPARSE) {
         const int vs = P.sp_vert_stride, B = P.sp_block_size;
         sp_klo = (L - 1) / B - P.sp_local_blocks;
@@ -456,13 +476,15 @@ phase1_kernel(const Phase1Params P) {
         int rall[kMaxHeadsPerGroup];   // every head's residue (lane c holds head c's)
 #pragma unroll
         for (int c = 0; c < kMaxHeadsPerGroup; ++c) rall[c] = __shfl(sp_res, c);
-        constexpr int TPT = kPartition / (WAVES * 64);   // tokens per thread
-        constexpr int TPU = 32 / TPT;                    // threads per 32-token unit
-        static_assert(kPartition % (WAVES * 64) == 0 && TPU >= 1 && TPU <= 64, "unit test layout");
+        constexpr int MW = WAVEIT ? 1 : WAVES;
+        constexpr int TPT = kPartition / (MW * 64);   // tokens per thread
+        constexpr int TPU = 32 / TPT;                 // threads per 32-token unit
+        static_assert(kPartition % (MW * 64) == 0 && TPU >= 1 && TPU <= 64, "unit test layout");
+        const int ti = WAVEIT ? lane : tid;
         bool hit = false;
 #pragma unroll
         for (int k = 0; k < TPT; ++k) {
-            const int t = start + tid * TPT + k;
+            const int t = start + ti * TPT + k;
             if (t < L) {
                 const int kb = t / B;
                 if (kb > sp_klo) {
@@ -475,16 +497,21 @@ phase1_kernel(const Phase1Params P) {
             }
         }
         const uint64_t bal = __ballot(hit);
-        if (lane == 0) {
-            uint32_t bits = 0;
+        uint32_t bits = 0;
 #pragma unroll
-            for (int j = 0; j < 64 / TPU; ++j)
-                if ((bal >> (j * TPU)) & (TPU == 64 ? ~0ull : ((1ull << TPU) - 1))) bits |= 1u << j;
-            s_umask[wv] = bits << (wv * (64 / TPU));
-        }
+        for (int j = 0; j < 64 / TPU; ++j)
+            if ((bal >> (j * TPU)) & (TPU == 64 ? ~0ull : ((1ull << TPU) - 1))) bits |= 1u << j;
+        if constexpr (WAVEIT) sp_um = __builtin_amdgcn_readfirstlane(bits);
+        else if (lane == 0) s_umask[wv] = bits << (wv * (64 / TPU));
     }
 
-    __syncthreads();   // block-table slice ready (and the attended-unit bits)
+    if constexpr (WAVEIT) {
+        // the wavefront's own slice: its LDS writes precede its reads in
+        // program order, and one wavefront's LDS accesses complete in order
+        __builtin_amdgcn_wave_barrier();
+    } else {
+        __syncthreads();   // block-table slice ready (and the attended-unit bits)
+    }
 
     const uint8_t *kc = P.key_cache + (int64_t)g * P.head_stride;
     const uint8_t *vc = P.value_cache + (int64_t)g * P.head_stride;
@@ -496,8 +523,27 @@ phase1_kernel(const Phase1Params P) {
     constexpr int UNIT = 32;
     constexpr int UPW = PREFIX ? kPrefixSlice / UNIT : (kPartition / UNIT) / WAVES;   // units per wavefront
     const int nunits = (n_tok + UNIT - 1) / UNIT;
+    // Wavefront items walk their attended units UPW at a time (chunks), the
+    // running max (pf_m), sums and output carried from chunk to chunk; the
+    // other schedules take their units in one pass.
+    float m = -INFINITY, lsum_r = 0.0f;
+    // (at least one chunk: an item no head attends runs one of unattended entries)
+    const int nchunks = WAVEIT ? max(1, (__builtin_popcount(sp_um) + UPW - 1) / UPW) : 1;
+    constexpr int RS = S::kD16 + 4;   // row stride (floats) of s_o
+    if constexpr (WAVEIT) {
+        pf_m = -INFINITY;
+        lsum = 0.0f;
+        osum = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int ck = 0;
+    do {
+    if constexpr (WAVEIT) {   // reloaded per chunk, not kept live across one
+        asm volatile("" : "+v"(qrow));
+        load_q();
+    }
     // Block-sparse: the wavefronts deal out the list of attended units
-    // (ascending) round-robin; entries past the list's end are -1.  Such an
+    // (ascending) round-robin (wavefront items: chunk ck of the wavefront's
+    // own list); entries past the list's end are -1.  Such an
     // entry still runs the unit's loads and matrix work, but every lane loads
     // the same few lines at the start of the pool (an address select, one
     // line per load instruction), its scores are -inf and its V words
@@ -505,7 +551,15 @@ phase1_kernel(const Phase1Params P) {
     // condition there costs the kernel about 120 VGPRs, i.e. its second
     // wavefront per SIMD.
     int sp_unit[SPARSE ? UPW : 1];
-    if constexpr (SPARSE) {
+    if constexpr (WAVEIT) {
+        uint32_t um = sp_um;
+        for (int i = 0; i < ck * UPW; ++i) um &= um - 1;   // skip the earlier chunks' units
+#pragma unroll
+        for (int u = 0; u < UPW; ++u) {
+            sp_unit[u] = um ? __builtin_ctz(um) : -1;
+            um &= um - 1;
+        }
+    } else if constexpr (SPARSE) {
         uint32_t um = 0;
 #pragma unroll
         for (int w2 = 0; w2 < WAVES; ++w2) um |= s_umask[w2];
@@ -547,11 +601,11 @@ phase1_kernel(const Phase1Params P) {
         if constexpr (BS >= 16) {
             // the tile's 16 tokens share one block: a wave-uniform block base
             // plus a per-lane offset that does not change between tiles
-            const int64_t b = __builtin_amdgcn_readfirstlane(s_bt[(t * UNIT + 16 * half) >> bs_log2]);
+            const int64_t b = __builtin_amdgcn_readfirstlane(s_btw[(t * UNIT + 16 * half) >> bs_log2]);
             const uint32_t lane_off = (uint32_t)((o & bs_mask) * 16 + (grp << (bs_log2 + 4)));
             base = kc + b * blk_stride + lane_off;
         } else {
-            const int64_t b = s_bt[o >> bs_log2];
+            const int64_t b = s_btw[o >> bs_log2];
             base = kc + b * blk_stride + (o & bs_mask) * 16 + (grp << (bs_log2 + 4));
         }
         if constexpr (SPARSE) base = uvalid(u) ? base : kc;
@@ -573,7 +627,7 @@ phase1_kernel(const Phase1Params P) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int tok = o + e;
-                tb[e] = vc + (int64_t)s_bt[tok >> bs_log2] * blk_stride + ((tok & bs_mask) + (col << bs_log2)) * KVB;
+                tb[e] = vc + (int64_t)s_btw[tok >> bs_log2] * blk_stride + ((tok & bs_mask) + (col << bs_log2)) * KVB;
                 if constexpr (SPARSE) tb[e] = uvalid(u) ? tb[e] : vc;
             }
 #pragma unroll
@@ -604,11 +658,11 @@ phase1_kernel(const Phase1Params P) {
         const uint8_t *base;
         if constexpr (BS >= 32) {
             // the unit's 32 tokens share one block
-            const int64_t b = __builtin_amdgcn_readfirstlane(s_bt[(t * UNIT) >> bs_log2]);
+            const int64_t b = __builtin_amdgcn_readfirstlane(s_btw[(t * UNIT) >> bs_log2]);
             const uint32_t lane_off = (uint32_t)(((o & bs_mask) + (col << bs_log2)) * KVB);
             base = vc + b * blk_stride + lane_off;
         } else {
-            const int64_t b = s_bt[o >> bs_log2];
+            const int64_t b = s_btw[o >> bs_log2];
             base = vc + b * blk_stride + (o & bs_mask) * KVB + (col << bs_log2) * KVB;
         }
         if constexpr (SPARSE) base = uvalid(u) ? base : vc;
@@ -673,7 +727,7 @@ phase1_kernel(const Phase1Params P) {
         return acc;
     };
 
-    if constexpr (!PREFIX) {
+    if constexpr (!PREFIX && !WAVEIT) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -759,14 +813,23 @@ phase1_kernel(const Phase1Params P) {
         }
     }
 
-    float m = -INFINITY;
+    m = -INFINITY;
 #pragma unroll
     for (int u = 0; u < UPW; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, sc[u][e]);
     m = wave_max(m);
     float mu = (m == -INFINITY) ? 0.0f : m;
-    if constexpr (PREFIX) {   // rescale the running state to the new running max
+    if constexpr (WAVEIT) {   // the running output: zero, or the earlier chunks' from the wavefront's LDS rows
+        const float *src = s_o + (wv * heads_alloc + col) * RS;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int row = 16 * dt + 4 * grp;
+            o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (ck > 0 && hvalid && row < D) o[dt] = *reinterpret_cast<const f32x4 *>(src + row);
+        }
+    }
+    if constexpr (PREFIX || WAVEIT) {   // rescale the running state to the new running max
         const float mn = fmaxf(pf_m, m);
         const float fo = mn == -INFINITY ? 1.0f : exp2_fast(pf_m - mn);
         pf_m = mn;
@@ -786,11 +849,11 @@ phase1_kernel(const Phase1Params P) {
     // carry P as hi + lo, two 16-bit parts (~16 significant bits).
     // The rounded weights' sum comes from one more MFMA pair per unit against
     // an all-ones A operand (every row of that tile is sum_t P[t][head]).
-    float lsum_r = 0.0f;
-    if constexpr (!PREFIX) lsum = 0.0f;
+    lsum_r = 0.0f;
+    if constexpr (!PREFIX && !WAVEIT) lsum = 0.0f;
     float pr[8];
     u32x4 ph = {0u, 0u, 0u, 0u}, pl = {0u, 0u, 0u, 0u};
-    if constexpr (!PREFIX) osum = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!PREFIX && !WAVEIT) osum = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t one2 = pack2<QDT == F32 ? BF16 : QDT>(1.0f, 1.0f);
     const u32x4 ones = {one2, one2, one2, one2};
     // Raw-word masks zeroing V of tokens past the sequence end (word w of a
@@ -880,13 +943,54 @@ phase1_kernel(const Phase1Params P) {
         }
         issue(j + PF);
     }
+    if constexpr (WAVEIT) {   // more chunks to come: park the running output in the wavefront's LDS rows
+        if (ck + 1 < nchunks && hvalid) {
+            float *dst = s_o + (wv * heads_alloc + col) * RS;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const int row = 16 * dt + 4 * grp;
+                if (row < D) *reinterpret_cast<f32x4 *>(dst + row) = o[dt];
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    } while (++ck < nchunks);   // chunks
+    if constexpr (WAVEIT) {
+        // the wavefront's own partition: statistics and normalised rows, in
+        // the merge's format (a head that attends nothing: -inf / 0 and a
+        // zero row)
+        lsum = wave_sum_groups(lsum);
+        const float lr = S::kF32 ? lsum : osum[0];
+        if (hvalid) {
+            const int64_t srow = (int64_t)s * P.num_heads + h0 + col;
+            const float inv = lr > 0.0f ? P.v_scale / lr : 0.0f;
+            uint8_t *base = reinterpret_cast<uint8_t *>(P.tmp_out) + (srow * maxP + p) * D * QB;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const int d0 = 16 * dt + 4 * grp;   // this lane's 4 consecutive head-dim elements
+                if (d0 < D) {
+                    const float r0 = o[dt][0] * inv, r1 = o[dt][1] * inv, r2 = o[dt][2] * inv, r3 = o[dt][3] * inv;
+                    if constexpr (QDT == F32)
+                        *reinterpret_cast<f32x4 *>(base + d0 * QB) = f32x4{r0, r1, r2, r3};
+                    else
+                        *reinterpret_cast<u32x2 *>(base + d0 * QB) = u32x2{pack2<QDT>(r0, r1), pack2<QDT>(r2, r3)};
+                }
+            }
+            if (grp == 0) {
+                float mabs = pf_m * kLn2;
+                if (P.alibi != nullptr) mabs += P.alibi[h0 + col] * (float)last;
+                P.max_logits[srow * maxP + p] = mabs;
+                P.exp_sums[srow * maxP + p] = lsum;
+            }
+        }
+        continue;
+    }
     if constexpr (PREFIX) continue;   // the running state stays in registers
     lsum = wave_sum_groups(lsum);
     if constexpr (S::kF32) lsum_r = lsum;
     else lsum_r = osum[0];
 
     // ---- merge the wavefronts through LDS ---------------------------------------
-    constexpr int RS = S::kD16 + 4;   // row stride (floats) of s_o
     if (hvalid) {
         if (grp == 0) {
             s_m[wv * kMaxHeadsPerGroup + col] = m;
@@ -1111,10 +1215,12 @@ hipError_t launch_sched(const Phase1Params &p, int lds, hipStream_t stream) {
     const hipError_t e = allow_lds(state, fn, dev, lds);
     if (e != hipSuccess) return e;
     int grid = (p.num_work + 7) / 8 * 8;
-    if (SCHED == 1) {
-        // at most kPhase1CompactRounds resident rounds of workgroups, each
-        // walking a balanced range of the used items
-        const int cap = p.compact_rounds * device_cu_count(dev) * resident_per_cu(state, fn, dev, WAVES * 64, lds);
+    if (SCHED == 1 || SCHED == 4) {
+        // at most p.compact_rounds resident rounds of workgroups (wavefront
+        // items: one round, each workgroup's range shared by its four
+        // wavefronts), each walking a balanced range of the used items
+        const int rounds = SCHED == 4 ? 1 : p.compact_rounds;
+        const int cap = rounds * device_cu_count(dev) * resident_per_cu(state, fn, dev, WAVES * 64, lds);
         grid = grid < cap ? grid : cap;
     } else if (SCHED == 2) {
         grid = p.num_work;   // one workgroup per (sequence, kv head, head group)
@@ -1143,10 +1249,10 @@ hipError_t launch_bs(const Phase1Params &p, int lds, hipStream_t stream) {
 
 template <int QDT, int KVDT, int D, bool SPARSE>
 hipError_t launch_one(const Phase1Params &p, int lds, hipStream_t stream) {
-    if constexpr (SPARSE) {   // block-sparse: the two-phase schedules only
+    if constexpr (SPARSE) {   // block-sparse: the dense grid, or the compact list taken by wavefront items
         switch (p.sched) {
         case 0: return launch_bs<QDT, KVDT, D, 0, true>(p, lds, stream);
-        case 1: return launch_bs<QDT, KVDT, D, 1, true>(p, lds, stream);
+        case 1: return launch_bs<QDT, KVDT, D, 4, true>(p, lds, stream);
         default: return hipErrorInvalidValue;
         }
     } else {
