@@ -269,6 +269,7 @@ def prefix_bench(args, dev):
         "dtype": c["dtype"], "data": "synthetic",
         "config": {"workload": "4 seqs x (16384 cached + 512 new tokens), H=24, kv_h=4 (GQA 6), d=256, bf16, "
                                "block 16", "num_seqs": 4, "context": 16384, "chunk": 512},
+        "timing": "mean of back-to-back launches (HIP events around each call)",
         "ms_min": round(mn, 5), "wall_ms_per_launch": round(wall, 5),
         "kv_GBps_if_read_once": round(kv_bytes / (mean * 1e-3) / 1e9, 1),
         "key_range_splits": int(splits), "workspace_bytes": int(ws_bytes),

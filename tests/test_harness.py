@@ -91,6 +91,21 @@ def test_prefix_summary_split_call(tmp_path):
     assert "prefix_merge_kernel" in text and "Key ranges per row block: 2" in text
 
 
+def test_prefix_summary_median(tmp_path):
+    # a clock transient over the first back-to-back calls raises the average;
+    # the summary also reports the rate at the per-dispatch median
+    t = _prefix_trace(1200.0, 30.0)
+    t["prefix"]["median_us"] = 1000.0
+    t["prefix_merge"]["median_us"] = 25.0
+    H.write_prefix_summary(str(tmp_path), t)
+    data = json.load(open(tmp_path / "prefix_attention.json"))
+    flops = bench.prefix_flops(**{k: bench.PREFIX_CASE[k] for k in ("ctx", "ql", "H", "d")})
+    assert abs(data["achieved_TFLOPs_median"] - flops / 1000e-6 / 1e12) < 1e-6
+    assert abs(data["achieved_TFLOPs_call_median"] - flops / 1025e-6 / 1e12) < 1e-6
+    assert abs(data["achieved_TFLOPs"] - flops / 1200e-6 / 1e12) < 1e-6
+    assert "| median (µs) |" in open(tmp_path / "prefix_attention.md").read()
+
+
 def test_bench_reads_traffic_only_for_current_sources():
     # every committed summary names the sources it was taken on; a lookup
     # returns bytes exactly when that hash is the current one
