@@ -128,7 +128,8 @@ void make_plan(const Shape &s, pav2_plan_t *pl) {
     pl->phase1_compact = compact ? 1 : 0;
     pl->phase1_rounds = compact ? pav2::phase1_compact_rounds(s.num_seqs) : 0;
     pl->phase1_xcd_classes = compact && pav2::phase1_xcd_classes(s.num_seqs, s.num_kv_heads, hg) ? 1 : 0;
-    pl->phase2_workgroups = pav2::phase2_workgroups((int64_t)s.num_seqs * s.num_heads, s.max_num_partitions);
+    pl->phase2_workgroups =
+        pav2::phase2_workgroups((int64_t)s.num_seqs * s.num_heads, s.max_num_partitions, s.head_size, s.qdt);
     {
         const int wpp = pav2::phase2_waves_per_pair(s.max_num_partitions);
         pl->phase2_threads = 64 * (wpp > 4 ? wpp : 4);

@@ -208,10 +208,22 @@ inline int phase2_waves_per_pair(int max_num_partitions) {
     return max_num_partitions > 128 ? 16 : (max_num_partitions > 64 ? 4 : 1);
 }
 
-inline int phase2_workgroups(int64_t pairs, int max_num_partitions) {
+// Short contexts with more (sequence, head) pairs than one resident round of
+// wavefronts (4 per SIMD on 256 compute units) give each wavefront two
+// pairs, 32 lanes each, so that every pair's chain of dependent reads runs in
+// one round (at the cost of one more row batch for the longest contexts).
+constexpr int64_t kPhase2OneRoundWaves = 256 * 16;
+inline int phase2_pairs_per_wave(int64_t pairs, int max_num_partitions, int head_size, int odt) {
+    const int lanes_per_row = head_size / (odt == F32 ? 4 : 8);   // a row must fit the pair's 32 lanes
+    return phase2_waves_per_pair(max_num_partitions) == 1 && pairs > kPhase2OneRoundWaves && lanes_per_row <= 32
+               ? 2 : 1;
+}
+inline int phase2_workgroups(int64_t pairs, int max_num_partitions, int head_size, int odt) {
     const int wpp = phase2_waves_per_pair(max_num_partitions);
+    const int ppw = phase2_pairs_per_wave(pairs, max_num_partitions, head_size, odt);
     const int wg_waves = wpp > 4 ? wpp : 4;
-    return (int)((pairs * wpp + wg_waves - 1) / wg_waves);
+    const int64_t waves = (pairs + ppw - 1) / ppw * wpp;
+    return (int)((waves + wg_waves - 1) / wg_waves);
 }
 
 }  // namespace pav2

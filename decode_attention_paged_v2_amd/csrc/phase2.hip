@@ -19,9 +19,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// One 16-byte word of a row (4 f32 or 8 16-bit elements) as floats.
 template <int ODT>
-__device__ __forceinline__ void load_vec(const uint8_t *src, float (&v)[ODT == F32 ? 4 : 8]) {
-    const u32x4 w = *reinterpret_cast<const u32x4 *>(src);
+__device__ __forceinline__ void to_vec(const u32x4 w, float (&v)[ODT == F32 ? 4 : 8]) {
     if constexpr (ODT == F32) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = as_f32(w[e]);
@@ -73,41 +73,49 @@ __device__ __forceinline__ void lse_merge(float &m, float &w, float m2, float w2
 }
 
 // WPP wavefronts per (sequence, head): 1 for short contexts (a workgroup
-// serves 4 pairs), 4 for long ones (one pair per workgroup).  A wavefront's
-// lanes form G groups of TPR lanes; lane (gi, r) owns VEC consecutive
-// head-dim elements r*VEC.. of the row and the partitions
-// q, q + Q, q + 2Q, ... with q = sub*G + gi and Q = WPP*G groups in all.
+// serves 4 pairs, or 8 with PPW = 2 pairs per wavefront, 32 lanes each), 4 or
+// 16 for long ones (one pair per workgroup).  A pair's LPP = 64 / PPW lanes
+// form G groups of TPR lanes; lane (gi, r) owns VEC consecutive head-dim
+// elements r*VEC.. of the row and the partitions q, q + Q, q + 2Q, ... with
+// q = sub*G + gi and Q = WPP*G groups in all.
 //   1. One pass over the used partitions' statistics gives the global
 //      (max M, sum W of exp(m_p - M) l_p) by an online merge; the first batch
 //      of tmp_output rows is loaded alongside it.
 //   2. Each lane accumulates exp(m_p - M) l_p * o_p over its partitions.
 //   3. Groups are added across lanes, then (WPP = 4) across wavefronts in LDS;
 //      the row is scaled by 1 / W and stored.
-template <int ODT, int D, int WPP>
-__global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const Phase2Params P) {
+template <int ODT, int D, int WPP, int PPW>
+__global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4))
+__attribute__((amdgpu_waves_per_eu(PPW == 2 ? 4 : 1))) phase2_kernel(const Phase2Params P) {
+    static_assert(PPW == 1 || (PPW == 2 && WPP == 1), "two pairs per wavefront: short contexts only");
     constexpr int VEC = ODT == F32 ? 4 : 8;
     constexpr int EB = ODT == F32 ? 4 : 2;
+    constexpr int LPP = 64 / PPW;                   // lanes per pair
     constexpr int TPR = D / VEC;                    // lanes per row
-    constexpr int G = 64 / TPR;                     // partition groups per wavefront
+    constexpr int G = LPP / TPR;                    // partition groups per pair and wavefront
     constexpr int Q = WPP * G;                      // partition groups per pair
-    constexpr int B = WPP == 4 ? 16 : 8;            // rows in flight per lane
+    constexpr int B = WPP == 4 ? 16 : (PPW == 2 ? 12 : 8);   // rows in flight per lane
     constexpr int WG_WAVES = WPP > 4 ? WPP : 4;
-    static_assert(D % VEC == 0 && TPR <= 64, "row split");
+    static_assert(D % VEC == 0 && TPR <= LPP, "row split");
     __shared__ float red[WPP > 1 ? WPP * D : 1];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int64_t gw = (int64_t)blockIdx.x * WG_WAVES + wv;
-    const int64_t sh = gw / WPP;                    // s * H + h
+    const int pb = PPW == 2 ? (lane & 32) : 0;     // the pair's first lane in the wavefront
+    const int pl = lane - pb;                       // lane within the pair
+    const int64_t sh = PPW == 2 ? gw * 2 + (pb >> 5) : gw / WPP;   // s * H + h
     const int sub = (int)(gw % WPP);
-    if (sh >= (int64_t)P.num_seqs * P.num_heads) return;   // uniform per workgroup when WPP > 1
+    // past the last pair: uniform per workgroup when WPP > 1, per pair (both
+    // halves of a wavefront are then done) when PPW = 2
+    if (sh >= (int64_t)P.num_seqs * P.num_heads) return;
     const int s = (int)(sh / P.num_heads);
     const int maxP = P.max_num_partitions;
     const int L = P.seq_lens[s];
     int np = (L + kPartition - 1) / kPartition;
     np = np < maxP ? np : maxP;
-    const int gi = lane / TPR;
-    const int r = lane - gi * TPR;
+    const int gi = pl / TPR;
+    const int r = pl - gi * TPR;
     const bool active = gi < G;
     const int q = sub * G + gi;
     uint8_t *out = reinterpret_cast<uint8_t *>(P.out) + (sh * D + r * VEC) * EB;
@@ -126,8 +134,10 @@ __global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const 
     const float *es = P.exp_sums + sh * maxP;
     const uint8_t *src = reinterpret_cast<const uint8_t *>(P.tmp_out) + (sh * maxP * D + r * VEC) * EB;
 
-    // A batch: B rows of this lane with their statistics, loaded together.
-    float v[B][VEC], bm[B], be[B];
+    // A batch: B rows of this lane with their statistics, loaded together;
+    // the rows stay as loaded (16-byte words) until they are accumulated.
+    u32x4 v[B];
+    float bm[B], be[B];
     auto load_batch = [&](int p0) {
 #pragma unroll
         for (int k = 0; k < B; ++k) {
@@ -135,7 +145,7 @@ __global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const 
             bm[k] = -INFINITY;
             be[k] = 0.0f;
             if (active && p < np) {
-                load_vec<ODT>(src + (int64_t)p * D * EB, v[k]);
+                v[k] = *reinterpret_cast<const u32x4 *>(src + (int64_t)p * D * EB);
                 bm[k] = ml[p];
                 be[k] = es[p];
             }
@@ -144,11 +154,11 @@ __global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const 
     load_batch(q);   // the first batch is in flight during the statistics pass
 
     float m = -INFINITY, w = 0.0f;
-    for (int p0 = lane; p0 < np; p0 += 4 * 64) {
+    for (int p0 = pl; p0 < np; p0 += 4 * LPP) {
         float sm[4], se[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int p = p0 + k * 64;
+            const int p = p0 + k * LPP;
             sm[k] = p < np ? ml[p] : -INFINITY;
             se[k] = p < np ? es[p] : 0.0f;
         }
@@ -156,7 +166,7 @@ __global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const 
         for (int k = 0; k < 4; ++k) lse_merge(m, w, sm[k], se[k]);
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
+    for (int off = LPP / 2; off > 0; off >>= 1) {   // within the pair's lanes
         const float m2 = __shfl_xor(m, off), w2 = __shfl_xor(w, off);
         lse_merge(m, w, m2, w2);
     }
@@ -169,8 +179,10 @@ __global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const 
         for (int k = 0; k < B; ++k) {
             if (be[k] != 0.0f) {   // rows past np (and inactive lanes) carry be = 0
                 const float wp = __builtin_amdgcn_exp2f((bm[k] - m) * kLog2e) * be[k];
+                float x[VEC];
+                to_vec<ODT>(v[k], x);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] += wp * v[k][e];
+                for (int e = 0; e < VEC; ++e) acc[e] += wp * x[e];
             }
         }
     };
@@ -179,10 +191,10 @@ __global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const 
         load_batch(p0);
         add_batch();
     }
-    // add the G groups of the wavefront (lanes r, r + TPR, ...)
-    if constexpr ((G & (G - 1)) == 0 && G * TPR == 64) {
+    // add the pair's G groups (lanes r, r + TPR, ... of the pair)
+    if constexpr ((G & (G - 1)) == 0 && G * TPR == LPP) {
 #pragma unroll
-        for (int off = TPR; off < 64; off <<= 1)
+        for (int off = TPR; off < LPP; off <<= 1)
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
     } else {
@@ -192,7 +204,7 @@ __global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const 
 #pragma unroll
         for (int k = 0; k < G; ++k)
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) t[e] += __shfl(acc[e], r + k * TPR);
+            for (int e = 0; e < VEC; ++e) t[e] += __shfl(acc[e], pb + r + k * TPR);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[e] = t[e];
     }
@@ -224,21 +236,27 @@ __global__ void __launch_bounds__(64 * (WPP > 4 ? WPP : 4)) phase2_kernel(const 
     }
 }
 
-template <int ODT, int D, int WPP>
+template <int ODT, int D, int WPP, int PPW>
 hipError_t launch_wpp(const Phase2Params &p, hipStream_t stream) {
     constexpr int WG_WAVES = WPP > 4 ? WPP : 4;
-    const int64_t waves = (int64_t)p.num_seqs * p.num_heads * WPP;
+    const int64_t pairs = (int64_t)p.num_seqs * p.num_heads;
+    const int64_t waves = (pairs + PPW - 1) / PPW * WPP;
     const dim3 grid((unsigned)((waves + WG_WAVES - 1) / WG_WAVES));
-    hipLaunchKernelGGL((phase2_kernel<ODT, D, WPP>), grid, dim3(64 * WG_WAVES), 0, stream, p);
+    hipLaunchKernelGGL((phase2_kernel<ODT, D, WPP, PPW>), grid, dim3(64 * WG_WAVES), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int ODT, int D>
 hipError_t launch_one(const Phase2Params &p, hipStream_t stream) {
     switch (phase2_waves_per_pair(p.max_num_partitions)) {
-    case 16: return launch_wpp<ODT, D, 16>(p, stream);
-    case 4: return launch_wpp<ODT, D, 4>(p, stream);
-    default: return launch_wpp<ODT, D, 1>(p, stream);
+    case 16: return launch_wpp<ODT, D, 16, 1>(p, stream);
+    case 4: return launch_wpp<ODT, D, 4, 1>(p, stream);
+    default:
+        if constexpr (D / (ODT == F32 ? 4 : 8) <= 32) {
+            if (phase2_pairs_per_wave((int64_t)p.num_seqs * p.num_heads, p.max_num_partitions, D, ODT) == 2)
+                return launch_wpp<ODT, D, 1, 2>(p, stream);
+        }
+        return launch_wpp<ODT, D, 1, 1>(p, stream);
     }
 }
 

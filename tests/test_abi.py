@@ -192,6 +192,20 @@ def test_plan(cfg, expect):
                                        (cfg["num_kv_heads"] * p["head_groups"]) % 8 == 0 else 0)
 
 
+@pytest.mark.parametrize("pairs,maxp,d,odt,expect", [
+    (4096, 8, 128, B.F16, 1024),     # one resident round of single-pair wavefronts
+    (4097, 8, 128, B.F16, 513),      # two pairs per wavefront: ceil(4097 / 2) waves, 4 per workgroup
+    (8192, 64, 80, B.F16, 1024),     # 256 ragged sequences x 32 heads
+    (8192, 65, 80, B.F16, 8192),     # 4 wavefronts per pair above 64 partitions: unchanged
+    (8192, 8, 256, B.F32, 2048),     # f32 rows of 64 lanes: one pair per wavefront
+    (8192, 8, 128, B.F32, 1024),     # f32 rows of 32 lanes fit a half-wavefront
+])
+def test_plan_phase2_pairs_per_wave(pairs, maxp, d, odt, expect):
+    p = pav2.plan(num_seqs=pairs, num_heads=1, num_kv_heads=1, head_size=d, block_size=16,
+                  max_num_partitions=maxp, query_dtype=odt, kv_cache_dtype=odt)
+    assert p["phase2_workgroups"] == expect
+
+
 @pytest.mark.parametrize("num_seqs,num_kv_heads,gqa,rounds,classes", [
     (4, 4, 6, 8, 0),      # a few long sequences: 8 resident rounds, items in order
     (15, 8, 4, 8, 0),     # just under the many-sequence bound

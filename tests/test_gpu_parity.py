@@ -305,6 +305,28 @@ def test_many_sequences_compact_classes(H, KVH, q, kv):
     compare(wl, g, run_oracle(wl))
 
 
+@pytest.mark.parametrize("S,H,KVH,D,q,kv", [
+    (1367, 3, 1, 80, "f16", "f16"),          # 4101 pairs (odd): the last wavefront holds one pair
+    (130, 32, 8, 128, "bf16", "bf16"),       # 4160 pairs
+    (1100, 4, 2, 64, "f32", "f32"),          # f32 rows of 16 lanes
+    (140, 32, 4, 256, "bf16", "fp8_e4m3"),   # a 32-lane row: one group per pair
+])
+def test_phase2_two_pairs_per_wavefront(S, H, KVH, D, q, kv):
+    """More (sequence, head) pairs than one resident round of wavefronts, short
+    contexts: phase 2 runs two pairs per wavefront.  Every pair is checked,
+    with empty sequences, one-partition and several-partition ones mixed."""
+    plan = pav2.plan(num_seqs=S, num_heads=H, num_kv_heads=KVH, head_size=D, block_size=16,
+                     max_num_partitions=4, query_dtype=B.F16, kv_cache_dtype=B.F16)
+    assert plan["phase2_workgroups"] == -(-(-(-S * H // 2)) // 4)
+    ks, vs = (0.05, 0.04) if kv == "fp8_e4m3" else (1.0, 1.0)
+    lens = lambda g: [int(x) for x in torch.randint(0, 2000, (S,), generator=g)]
+    spec = W.Spec(f"p2pairs_{S}_{H}", H, KVH, D, 16, q, kv, lens, pool=lambda n: n + 5, alibi=(D == 80),
+                  k_scale=ks, v_scale=vs, seed=S + H)
+    wl = W.generate(spec, poison=True)
+    g = run_gpu(wl.to(DEV))
+    compare(wl, g, run_oracle(wl))
+
+
 @pytest.mark.parametrize("BS", [1, 2, 4, 8, 32, 64, 128, 256, 512])
 def test_edge_block_sizes(BS):
     spec = W.Spec(f"bs{BS}", 8, 2, 128, BS, "f16", "f16", lambda g: [1, max(BS - 1, 0), BS, BS + 1, 1300, 0, 7],
