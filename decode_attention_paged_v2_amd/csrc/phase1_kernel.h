@@ -155,11 +155,14 @@ __device__ __forceinline__ T load_stream(const uint8_t *p) {
 
 // SCHED: 0 dense grid of partition slots, 1 compact list of used partitions,
 // 2 single pass (one workgroup per (sequence, kv head, head group) walks all
-// of the sequence's partitions and writes the final output).
+// of the sequence's partitions and writes the final output), 3 paged prefix
+// attention (the layout kept for f32 queries and head sizes the MFMA prefix
+// kernel does not cover), 4 the compact list taken by wavefront items
+// (block-sparse only; at most 256 VGPRs, two wavefronts per SIMD).
 // BS: the block size when fixed at compile time (16 or 32), 0 for any of
 // 8 .. 512, -1 for 1, 2 or 4 (a lane's 8-token V slice then spans blocks).
-// SPARSE: the block-sparse pattern of Phase1Params (dense and compact
-// schedules only): units of a partition that no head of the group attends
+// SPARSE: the block-sparse pattern of Phase1Params (the dense grid and
+// wavefront items): units of a partition that no head of the group attends
 // are never loaded, and scores of tokens a head does not attend are masked.
 template <int QDT, int KVDT, int D, int WAVES, int SCHED, int BS, bool SPARSE>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SCHED == 4 ? 2 : kPhase1Occupancy)))

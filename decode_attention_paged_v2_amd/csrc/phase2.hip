@@ -8,8 +8,9 @@
 // reduce would divide 0 by 0 there).  There is no cap on the partition count
 // (page 2 truncates past 1024).
 //
-// Short contexts: one wavefront per (sequence, head); long contexts: one
-// 4-wavefront workgroup per (sequence, head).  See phase2_kernel.
+// Short contexts: one wavefront per (sequence, head), or two pairs per
+// wavefront when the pairs outnumber one resident round of wavefronts; long
+// contexts: 4 or 16 wavefronts per (sequence, head).  See phase2_kernel.
 #include <math.h>
 
 #include "pav2_internal.h"

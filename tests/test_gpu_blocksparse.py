@@ -11,6 +11,7 @@ import torch
 import oracle
 import _tol
 import decode_attention_paged_v2_amd as pav2
+from decode_attention_paged_v2_amd import _binding as B
 from decode_attention_paged_v2_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -132,6 +133,20 @@ def test_blocksparse_many_sequences_compact_classes(H, KVH):
     wl = make(LENS + [700, 90, 1536, 0, 33, 2000, 511, 4, 1025, 260, 1700, 3000], H=H, KVH=KVH, D=64, q="f16",
               kv="f16", alibi=True, seed=H + KVH)
     assert wl.num_seqs == 20
+    compare(wl, run_gpu(wl, sp), run_oracle(wl, sp))
+
+
+def test_blocksparse_phase2_two_pairs_per_wavefront():
+    """4480 (sequence, head) pairs with short contexts: phase 2 runs two pairs
+    per wavefront; with no local window and a stride of 4, short sequences
+    leave some heads nothing to attend (zero rows, weight 0 everywhere)."""
+    sp = (0, 0, 4, 16, 1)
+    g = torch.Generator().manual_seed(77)
+    lens = [int(x) for x in torch.randint(0, 1500, (140,), generator=g)]
+    wl = make(lens, H=32, KVH=8, D=64, q="f16", kv="f16", seed=78)
+    plan = pav2.plan(num_seqs=140, num_heads=32, num_kv_heads=8, head_size=64, block_size=16,
+                     max_num_partitions=wl.max_num_partitions, query_dtype=B.F16, kv_cache_dtype=B.F16)
+    assert plan["phase2_workgroups"] == 4480 // 2 // 4
     compare(wl, run_gpu(wl, sp), run_oracle(wl, sp))
 
 
