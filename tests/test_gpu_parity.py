@@ -319,7 +319,9 @@ def test_phase2_two_pairs_per_wavefront(S, H, KVH, D, q, kv):
                      max_num_partitions=4, query_dtype=B.F16, kv_cache_dtype=B.F16)
     assert plan["phase2_workgroups"] == -(-(-(-S * H // 2)) // 4)
     ks, vs = (0.05, 0.04) if kv == "fp8_e4m3" else (1.0, 1.0)
-    lens = lambda g: [int(x) for x in torch.randint(0, 2000, (S,), generator=g)]
+    # every 97th sequence empty and every 89th a single token, the rest random
+    lens = lambda g: [0 if i % 97 == 5 else (1 if i % 89 == 7 else int(x))
+                      for i, x in enumerate(torch.randint(0, 2000, (S,), generator=g))]
     spec = W.Spec(f"p2pairs_{S}_{H}", H, KVH, D, 16, q, kv, lens, pool=lambda n: n + 5, alibi=(D == 80),
                   k_scale=ks, v_scale=vs, seed=S + H)
     wl = W.generate(spec, poison=True)
