@@ -48,7 +48,7 @@ def assert_close(out, ref, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [64, 80, 128, 256])
+@pytest.mark.parametrize("d", [64, 80, 96, 112, 120, 128, 192, 256])   # MFMA kernel: 64, 96, 128, 192, 256 (16-bit)
 def test_prefix_matches_oracle(dtype, d):
     print(f"case prefix {dtype} d={d}", flush=True)
     # contexts: none, under one tile, one partition, several partitions; chunks of 1 .. 70 tokens, one empty
@@ -118,6 +118,8 @@ def _prefix_call(g, ql, ctx, scale, workspace):
     ("bf16", 256, [3000], [40], 8, 1),               # 3 row blocks over 48 tiles: 8 key ranges
     ("f16", 128, [2100, 0, 64, 900], [30, 50, 1, 7], 12, 4),   # ragged: empty ranges, rows before a range
     ("bf16", 64, [5000, 40], [3, 90], 16, 2),
+    ("f16", 192, [2500], [20], 6, 1),                # merge columns not a multiple of the 16-lane step
+    ("bf16", 96, [4000, 100], [10, 30], 8, 2),
 ])
 def test_prefix_key_ranges_split(dtype, d, ctx, ql, H, KVH):
     """Few row blocks over long contexts: the call splits each row block's keys

@@ -138,7 +138,7 @@ EDGE_LENS = [0, 1, 2, 15, 16, 17, 511, 512, 513, 1000, 1536, 0, 2049]
 
 @pytest.mark.parametrize("q,kv", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
                                   ("f32", "fp8_e4m3"), ("f16", "fp8_e4m3"), ("bf16", "fp8_e4m3")])
-@pytest.mark.parametrize("D", [64, 80, 120, 128, 256])
+@pytest.mark.parametrize("D", [64, 80, 96, 112, 120, 128, 192, 256])
 def test_v1_edge_dtypes_head_sizes(q, kv, D):
     if kv == "fp8_e4m3" and D % 16:
         pytest.skip("head size not a multiple of 16 fp8 elements")
