@@ -111,7 +111,8 @@ def _announce(request):
 @pytest.mark.parametrize("sp", PATTERNS)
 @pytest.mark.parametrize("q,kv,D,alibi", [("bf16", "bf16", 128, False), ("f16", "f16", 80, True),
                                           ("f32", "f32", 64, True), ("bf16", "fp8_e4m3", 256, False),
-                                          ("f16", "fp8_e4m3", 112, True)])
+                                          ("f16", "fp8_e4m3", 112, True), ("bf16", "bf16", 192, True),
+                                          ("f16", "f16", 96, False), ("f32", "f32", 120, False)])
 def test_blocksparse_matches_oracle(sp, q, kv, D, alibi):
     wl = make(LENS, H=8, KVH=2, D=D, q=q, kv=kv, alibi=alibi, seed=sp[3] + D)
     g = run_gpu(wl, sp)

@@ -101,6 +101,22 @@ def test_write_matches_oracle(in_dt, cache_dt, d, pattern):
     assert_same_bytes(gv, rv)
 
 
+@pytest.mark.parametrize("in_dt,cache_dt", PAIRS)
+@pytest.mark.parametrize("d", [96, 112, 120, 192])
+def test_write_other_head_sizes(in_dt, cache_dt, d):
+    """The remaining supported head sizes, each through a prefill and a padded slot pattern."""
+    print(f"case {in_dt}->{cache_dt} d={d}", flush=True)
+    if cache_dt == "fp8_e4m3" and d % 16:
+        pytest.skip("fp8 caches need head_size % 16 == 0")
+    scaled = cache_dt == "fp8_e4m3"
+    for pattern in ("prefill", "padded"):
+        gk, gv, rk, rv = run_both(in_dt, cache_dt, T=150, kvh=2, d=d, bs=16, nb=30, pattern=pattern,
+                                  k_scale=0.05 if scaled else 1.0, v_scale=0.04 if scaled else 1.0,
+                                  seed=d + 1, mag=30.0 if scaled else 1.0)
+        assert_same_bytes(gk, rk)
+        assert_same_bytes(gv, rv)
+
+
 @pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 64, 512])
 @pytest.mark.parametrize("in_dt,cache_dt", [("bf16", "bf16"), ("f16", "fp8_e4m3"), ("f32", "f32")])
 def test_write_block_sizes(bs, in_dt, cache_dt):
